@@ -1,0 +1,469 @@
+"""Pins for the CPU oracle (no GPU).
+
+Each test ties the oracle to something other than itself: hand-derived values of
+the E4M3 definition (tests/golden), torch's own float8_e4m3fn / bfloat16 casts (an
+independent library implementation of the same formats), closed forms, exact
+invariants, an integer formulation of the GEMM and lossless special cases.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _f32_bits(x):
+    return int(np.float32(x).view(np.uint32))
+
+
+def _torch_decode(codes: np.ndarray) -> np.ndarray:
+    t = torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8)).view(torch.float8_e4m3fn)
+    return t.to(torch.float64).numpy()
+
+
+def _torch_encode(v: np.ndarray) -> np.ndarray:
+    t = torch.from_numpy(np.ascontiguousarray(v, dtype=np.float32)).to(torch.float8_e4m3fn)
+    return t.view(torch.uint8).numpy()
+
+
+# ------------------------------------------------------------------------------ decode
+
+def test_decode_landmarks_golden(oracle_lib):
+    for lm in _load("e4m3_landmarks.json")["landmarks"]:
+        code = int(lm["code"], 16)
+        got = oracle.e4m3_decode(code)
+        if lm["value"] == "nan":
+            assert math.isnan(got), lm
+        else:
+            want = float.fromhex(lm["value"]) if "0x" in lm["value"] else float(lm["value"])
+            assert got == want and math.copysign(1, got) == math.copysign(1, want), lm
+
+
+def test_decode_structure_all_codes(oracle_lib):
+    v = oracle.e4m3_decode_all()
+    nan_codes = [c for c in range(256) if math.isnan(v[c])]
+    assert nan_codes == [0x7F, 0xFF]
+    pos = v[:0x7F]
+    assert np.all(np.diff(pos) > 0), "positive codes must be strictly increasing"
+    assert pos[0x7E] == 448.0 and pos[0x01] == 2.0 ** -9 and pos[0x08] == 2.0 ** -6
+    for c in range(0x7F):
+        assert v[c | 0x80] == -v[c]
+        assert math.copysign(1.0, v[c | 0x80]) == -1.0
+    # every finite E4M3 value is an integer multiple of 2^-9 and a bf16 value
+    fin = v[~np.isnan(v)]
+    assert np.all(np.mod(fin * 512.0, 1.0) == 0.0)
+    assert np.all(np.float32(fin).astype(np.float64) == fin)
+
+
+def test_decode_matches_torch_float8(oracle_lib):
+    v = oracle.e4m3_decode_all()
+    t = _torch_decode(np.arange(256, dtype=np.uint8))
+    both_nan = np.isnan(v) & np.isnan(t)
+    assert np.array_equal(np.isnan(v), np.isnan(t))
+    assert np.all((v == t) | both_nan)
+    assert np.array_equal(np.signbit(v[~both_nan]), np.signbit(t[~both_nan]))
+
+
+# ------------------------------------------------------------------------------ encode
+
+def test_encode_roundtrip_finite_codes(oracle_lib):
+    v = oracle.e4m3_decode_all()
+    for c in range(256):
+        if c in (0x7F, 0xFF):
+            continue
+        assert oracle.e4m3_encode(v[c]) == c, hex(c)
+
+
+def test_encode_midpoints_ties_to_even(oracle_lib):
+    v = oracle.e4m3_decode_all()
+    for c in range(0x7E):
+        lo, hi = v[c], v[c + 1]
+        mid = np.float32((lo + hi) / 2)          # 5 significant bits: exact in fp32
+        assert float(mid) == (lo + hi) / 2
+        even = c if c % 2 == 0 else c + 1
+        assert oracle.e4m3_encode(mid) == even, (hex(c), float(mid))
+        assert oracle.e4m3_encode(-mid) == even | 0x80
+        below = np.nextafter(mid, np.float32(0))
+        above = np.nextafter(mid, np.float32(np.inf))
+        assert oracle.e4m3_encode(below) == c
+        assert oracle.e4m3_encode(above) == c + 1
+
+
+def test_encode_saturation_nan_and_signed_zero(oracle_lib):
+    for x in [448.0, 449.0, 463.99, 464.0, 480.0, 1e30, np.inf]:
+        assert oracle.e4m3_encode(x) == 0x7E
+        assert oracle.e4m3_encode(-x) == 0xFE
+    assert oracle.e4m3_encode(np.nan) in (0x7F, 0xFF)
+    assert oracle.e4m3_encode(-0.0) == 0x80
+    assert oracle.e4m3_encode(-1e-30) == 0x80
+    assert oracle.e4m3_encode(1e-30) == 0x00
+    assert oracle.e4m3_encode(2.0 ** -10) == 0x00          # tie 0 | 2^-9 -> even (0)
+    assert oracle.e4m3_encode(np.nextafter(np.float32(2.0 ** -10), np.float32(1))) == 0x01
+
+
+def test_encode_matches_torch_cast_on_dense_sample(oracle_lib):
+    # torch's float32 -> float8_e4m3fn cast is round-to-nearest-even; it does not
+    # saturate, so compare only below the overflow threshold (464).
+    top = int(np.float32(463.9).view(np.uint32))
+    bits = np.arange(0, top, 97, dtype=np.uint32)            # ~11.4M patterns, all binades
+    rng = np.random.Generator(np.random.PCG64(7))
+    bits = np.concatenate([bits, rng.integers(0, top, size=1 << 20, dtype=np.uint32)])
+    vals = bits.view(np.float32)
+    vals = np.concatenate([vals, -vals])
+    assert np.array_equal(oracle.e4m3_encode_array(vals), _torch_encode(vals))
+
+
+def test_encode_matches_torch_cast_near_every_midpoint(oracle_lib):
+    v = oracle.e4m3_decode_all()[:0x7F]
+    mids = np.float32((v[:-1] + v[1:]) / 2)
+    pts = [mids]
+    x = mids.copy()
+    y = mids.copy()
+    for _ in range(8):
+        x = np.nextafter(x, np.float32(0))
+        y = np.nextafter(y, np.float32(np.inf))
+        pts += [x.copy(), y.copy()]
+    vals = np.concatenate(pts + [np.float32(v)])
+    vals = np.concatenate([vals, -vals])
+    assert np.array_equal(oracle.e4m3_encode_array(vals), _torch_encode(vals))
+
+
+# ------------------------------------------------------------------------------ bf16
+
+def test_f32_to_bf16_matches_torch(oracle_lib):
+    rng = np.random.Generator(np.random.PCG64(3))
+    bits = rng.integers(0, 0x7F800000, size=1 << 20, dtype=np.uint32)
+    special = np.array([0x7F7F7FFF, 0x7F7F8000, 0x7F7F8001, 0x7F7FFFFF, 0x00000001, 0x00008000,
+                        0x00018000, 0x3F808000, 0x3F818000, 0x00000000], dtype=np.uint32)
+    bits = np.concatenate([bits, special])
+    v = bits.view(np.float32)
+    v = np.concatenate([v, -v])
+    want = torch.from_numpy(v.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(oracle.f32_to_bf16_array(v), want)
+
+
+# ------------------------------------------------------------------------------ act quant
+
+def _golden_tile(spec):
+    t = np.zeros(128, dtype=np.uint16)
+    for i, h in spec:
+        t[i] = int(h, 16)
+    return t
+
+
+def test_act_quant_golden_cases(oracle_lib):
+    cases = _load("act_quant_cases.json")["cases"]
+    x = np.stack([_golden_tile(c["tile"]) for c in cases])
+    q, s = oracle.act_quant(x)
+    for i, c in enumerate(cases):
+        assert int(s[i, 0].view(np.uint32)) == int(c["scale_bits"], 16), c["name"]
+        for idx, code in c["codes"]:
+            assert q[i, idx] == int(code, 16), (c["name"], idx)
+
+
+def _torch_act_quant(x_bits: np.ndarray):
+    """Same steps expressed with torch CPU ops and torch's own E4M3 cast."""
+    x = torch.from_numpy(x_bits.view(np.int16)).view(torch.bfloat16).float()
+    M, K = x.shape
+    t = x.reshape(M, K // 128, 128)
+    amax = t.abs().amax(dim=-1, keepdim=True)
+    s = amax / 448.0
+    d = torch.where(amax == 0, torch.ones_like(s), s)
+    q = (t / d).to(torch.float8_e4m3fn).view(torch.uint8).reshape(M, K)
+    return q.numpy(), s.reshape(M, K // 128).numpy()
+
+
+@pytest.mark.parametrize("M,K,seed", [(37, 512, 0), (5, 128, 1), (64, 256, 2)])
+def test_act_quant_matches_torch_steps(oracle_lib, M, K, seed):
+    x = synth.random_bf16((M, K), seed)
+    q, s = oracle.act_quant(x)
+    tq, ts = _torch_act_quant(x)
+    assert np.array_equal(q, tq)
+    assert np.array_equal(s.view(np.uint32), ts.view(np.uint32))
+
+
+def test_act_quant_special_tiles_match_torch_steps(oracle_lib):
+    x = synth.special_tiles()
+    q, s = oracle.act_quant(x)
+    tq, ts = _torch_act_quant(x)
+    assert np.array_equal(q, tq)
+    assert np.array_equal(s.view(np.uint32), ts.view(np.uint32))
+
+
+def test_act_quant_invariants(oracle_lib):
+    x = synth.random_bf16((64, 1024), 11)
+    q, s = oracle.act_quant(x)
+    xf = oracle.bf16_to_f32_array(x).reshape(64, 8, 128)
+    qt = q.reshape(64, 8, 128)
+    amax = np.abs(xf).max(axis=-1)
+    # scale: IEEE fp32 amax/448, re-derived through float64 (double rounding of a
+    # quotient through 53 >= 2*24+2 bits is innocuous)
+    assert np.array_equal(s, np.float32(amax.astype(np.float64) / 448.0))
+    # the amax element codes to +-448
+    idx = np.abs(xf).argmax(axis=-1)
+    codes = np.take_along_axis(qt, idx[..., None], axis=-1)[..., 0]
+    assert np.all((codes & 0x7F) == 0x7E)
+    # sign of every code equals the sign bit of the input
+    assert np.array_equal(qt >> 7, (x.reshape(64, 8, 128) >> 15).astype(np.uint8))
+    # |decode(q) - x/s| <= half an E4M3 ulp at that magnitude
+    dec = oracle.e4m3_decode_all()[qt]
+    quo = xf.astype(np.float64) / s[..., None].astype(np.float64)
+    e = np.floor(np.log2(np.maximum(np.abs(dec), 2.0 ** -6)))
+    half_ulp = 2.0 ** (e - 4)
+    assert np.all(np.abs(dec - quo) <= half_ulp * (1 + 1e-6))
+
+
+@pytest.mark.parametrize("k", [-40, -3, 1, 7, 60])
+def test_act_quant_power_of_two_invariance(oracle_lib, k):
+    # Scaling a tile by 2^k (no overflow/underflow) keeps every code and scales the
+    # scale by exactly 2^k.
+    x = synth.random_bf16((16, 256), 5)
+    xf = oracle.bf16_to_f32_array(x)
+    x2 = synth.bf16_bits(np.float32(xf * np.float32(2.0 ** k)))
+    assert np.array_equal(oracle.bf16_to_f32_array(x2), np.float32(xf * 2.0 ** k))
+    q1, s1 = oracle.act_quant(x)
+    q2, s2 = oracle.act_quant(x2)
+    assert np.array_equal(q1, q2)
+    assert np.array_equal(s2, np.float32(s1 * np.float32(2.0 ** k)))
+
+
+def test_act_quant_zero_tiles(oracle_lib):
+    x = np.zeros((3, 256), dtype=np.uint16)
+    x[1, 3] = 0x8000
+    x[2, 130:140] = 0x8000
+    q, s = oracle.act_quant(x)
+    assert np.all(s == 0) and not np.any(np.signbit(s))
+    assert np.array_equal(q, (x >> 8).astype(np.uint8))
+
+
+# ------------------------------------------------------------------------------ weight quant
+
+def _torch_weight_quant(w_bits: np.ndarray):
+    w = torch.from_numpy(w_bits.view(np.int16)).view(torch.bfloat16).float()
+    N, K = w.shape
+    nnb = (N + 127) // 128
+    pad = torch.zeros(nnb * 128, K)
+    pad[:N] = w
+    t = pad.reshape(nnb, 128, K // 128, 128)
+    amax = t.abs().amax(dim=(1, 3), keepdim=True)
+    s = amax / 448.0
+    d = torch.where(amax == 0, torch.ones_like(s), s)
+    q = (t / d).to(torch.float8_e4m3fn).view(torch.uint8).reshape(nnb * 128, K)[:N]
+    return q.numpy(), s.reshape(nnb, K // 128).numpy()
+
+
+@pytest.mark.parametrize("N,K", [(256, 256), (200, 384), (64, 128), (576, 256), (1, 128)])
+def test_weight_quant_matches_torch_steps(oracle_lib, N, K):
+    w = synth.random_bf16((N, K), N + K, std=0.02)
+    q, s = oracle.weight_quant(w)
+    tq, ts = _torch_weight_quant(w)
+    assert s.shape == ((N + 127) // 128, K // 128)
+    assert np.array_equal(q, tq)
+    assert np.array_equal(s.view(np.uint32), ts.view(np.uint32))
+
+
+def test_weight_quant_ragged_block_uses_valid_rows_only(oracle_lib):
+    # N = 130: block row 1 has two valid rows; its amax must come from those rows.
+    w = np.zeros((130, 128), dtype=np.uint16)
+    w[:128] = 0x4460          # 896 in the full block
+    w[128, 0] = 0x40E0        # 7.0 -> scale 2^-6 in the ragged block
+    q, s = oracle.weight_quant(w)
+    assert s[0, 0] == np.float32(2.0) and s[1, 0] == np.float32(2.0 ** -6)
+    assert q[128, 0] == 0x7E and np.all(q[:128] == 0x7E)
+
+
+def test_weight_quant_equals_act_quant_on_one_row_blocks(oracle_lib):
+    # With N = 1 every 128x128 block holds a single row: the block quantiser must then
+    # agree exactly with the 1x128 activation quantiser.
+    x = synth.random_bf16((1, 1024), 21)
+    qa, sa = oracle.act_quant(x)
+    qw, sw = oracle.weight_quant(x)
+    assert np.array_equal(qa, qw) and np.array_equal(sa, sw)
+
+
+# ------------------------------------------------------------------------------ dequant
+
+def test_dequant_unit_scale_is_exact_decode(oracle_lib):
+    q = np.tile(np.arange(256, dtype=np.uint8), (130, 1))[:, :256]
+    q[q == 0x7F] = 0
+    q[q == 0xFF] = 0
+    s = np.ones((2, 2), dtype=np.float32)
+    w = oracle.weight_dequant(q, s)
+    dec = oracle.e4m3_decode_all()[q]
+    assert np.array_equal(oracle.bf16_to_f32_array(w).astype(np.float64), dec)
+    assert np.array_equal(np.signbit(oracle.bf16_to_f32_array(w)), np.signbit(dec))
+
+
+@pytest.mark.parametrize("N,K", [(200, 384), (576, 256)])
+def test_dequant_matches_torch(oracle_lib, N, K):
+    w0 = synth.random_bf16((N, K), 99, std=0.02)
+    q, s = oracle.weight_quant(w0)
+    w = oracle.weight_dequant(q, s)
+    tq = torch.from_numpy(q).view(torch.float8_e4m3fn).float()
+    ts = torch.from_numpy(s).repeat_interleave(128, 0)[:N].repeat_interleave(128, 1)
+    want = (tq * ts).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(w, want)
+
+
+# ------------------------------------------------------------------------------ GEMM
+
+def test_gemm_golden_small(oracle_lib):
+    g = _load("gemm_small.json")
+    M, N, K = g["M"], g["N"], g["K"]
+
+    def rows(spec):
+        out = np.zeros((len(spec["rows"]), K), dtype=np.uint16)
+        for i, r in enumerate(spec["rows"]):
+            out[i] = int(r["fill"], 16)
+            for k, h in r["set"]:
+                out[i, k] = int(h, 16)
+        return out
+
+    A, W = rows(g["A"]), rows(g["W"])
+    aq, sa = oracle.act_quant(A)
+    wq, sw = oracle.weight_quant(W)
+    assert [[hex(int(v))] for v in sa.view(np.uint32)[:, 0]] == g["sa_bits"]
+    assert hex(int(sw.view(np.uint32)[0, 0])) == g["sw_bits"][0][0]
+    assert np.all(wq[0] == int(g["W_codes"]["row0_all"], 16))
+    assert wq[1, 0] == int(g["W_codes"]["row1_k0"], 16)
+    y, b = oracle.block_gemm(aq, sa, wq, sw)
+    assert np.array_equal(y, np.array(g["Y"]))
+    assert np.array_equal(b, np.array(g["bound"]))
+
+
+def _int_gemm(aq, sa, wq, sw):
+    """Integer formulation: E4M3 codes times 2^9 are integers, so each slice partial is
+    an exact int64 matmul; y = sum_kb (P_kb * 2^-18) * (sa * sw) in float64."""
+    dec = oracle.e4m3_decode_all()
+    dec[np.isnan(dec)] = 0
+    ai = (dec[aq] * 512).astype(np.int64)
+    wi = (dec[wq] * 512).astype(np.int64)
+    M, K = aq.shape
+    N = wq.shape[0]
+    y = np.zeros((M, N), dtype=np.float64)
+    nb = np.arange(N) // 128
+    for kb in range(K // 128):
+        sl = slice(kb * 128, (kb + 1) * 128)
+        p = (ai[:, sl] @ wi[:, sl].T).astype(np.float64) * 2.0 ** -18
+        f = sa[:, kb].astype(np.float64)[:, None] * sw[nb, kb].astype(np.float64)[None, :]
+        y += p * f
+    return y
+
+
+@pytest.mark.parametrize("M,N,K", [(64, 256, 256), (33, 200, 384), (5, 576, 128)])
+def test_gemm_matches_integer_formulation(oracle_lib, M, N, K):
+    A = synth.random_bf16((M, K), 1)
+    W = synth.random_bf16((N, K), 2, std=0.02)
+    aq, sa = oracle.act_quant(A)
+    wq, sw = oracle.weight_quant(W)
+    y, b = oracle.block_gemm(aq, sa, wq, sw)
+    assert np.array_equal(y, _int_gemm(aq, sa, wq, sw))
+    # bound = sum_k |a_k w_k| over the dequantised operands (float64 matmul, own order)
+    dec = oracle.e4m3_decode_all()
+    ad = np.abs(dec[aq]) * np.repeat(sa.astype(np.float64), 128, axis=1)
+    wd = np.abs(dec[wq]) * np.repeat(sw.astype(np.float64), 128, axis=1)[np.arange(N) // 128]
+    assert np.allclose(b, ad @ wd.T, rtol=1e-12, atol=0)
+    assert np.all(np.abs(y) <= b * (1 + 1e-12))
+
+
+def test_gemm_sampled_equals_full(oracle_lib):
+    A = synth.random_bf16((40, 256), 3)
+    W = synth.random_bf16((300, 256), 4, std=0.02)
+    aq, sa = oracle.act_quant(A)
+    wq, sw = oracle.weight_quant(W)
+    y, b = oracle.block_gemm(aq, sa, wq, sw)
+    r, c = synth.sample_outputs(40, 300, 500, seed=9)
+    ys, bs = oracle.block_gemm_sampled(aq, sa, wq, sw, r, c)
+    assert np.array_equal(ys, y[r, c]) and np.array_equal(bs, b[r, c])
+
+
+def test_gemm_one_hot_rows(oracle_lib):
+    # A row with a single non-zero at k0 quantises to +-448 at k0 and zero scales
+    # elsewhere, so y[n] = +-448 * sa[k0/128] * sw[n/128, k0/128] * decode(wq[n, k0]).
+    M, N, K = 6, 300, 512
+    A = np.zeros((M, K), dtype=np.uint16)
+    ks = [0, 127, 128, 300, 383, 511]
+    vals = [0x3F80, 0xC2F6, 0x0003, 0x7F7F, 0xBC00, 0x4123]
+    for m, (k0, v) in enumerate(zip(ks, vals)):
+        A[m, k0] = v
+    W = synth.random_bf16((N, K), 8, std=0.02)
+    aq, sa = oracle.act_quant(A)
+    wq, sw = oracle.weight_quant(W)
+    y, b = oracle.block_gemm(aq, sa, wq, sw)
+    dec = oracle.e4m3_decode_all()
+    for m, k0 in enumerate(ks):
+        sign = -1.0 if A[m, k0] & 0x8000 else 1.0
+        assert aq[m, k0] == (0xFE if sign < 0 else 0x7E)
+        kb = k0 // 128
+        want = (sign * 448.0 * dec[wq[:, k0]]) * (np.float64(sa[m, kb]) * sw[np.arange(N) // 128, kb].astype(np.float64))
+        assert np.array_equal(y[m], want)
+        assert np.array_equal(b[m], np.abs(want))
+
+
+def test_gemm_lossless_inputs_equal_float64_matmul(oracle_lib):
+    # Every A tile / W block is (E4M3 values) x 2^e with its max |.| = 448 * 2^e, so
+    # quantisation is lossless and the block-scaled GEMM must equal the float64 matmul of
+    # the original inputs exactly (exponents kept small so that matmul is exact too).
+    rng = np.random.Generator(np.random.PCG64(12))
+    dec = oracle.e4m3_decode_all()
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    M, N, K = 48, 260, 256
+    ca = rng.choice(finite, size=(M, K))
+    cw = rng.choice(finite, size=(N, K))
+    ca[:, ::128] = 0x7E          # pin every tile's max to 448
+    cw[::128, ::128] = 0xFE      # and every block's max to 448 (negative)
+    ea = rng.integers(-2, 3, size=(M, K // 128))
+    ew = rng.integers(-2, 3, size=((N + 127) // 128, K // 128))
+    a64 = dec[ca] * np.repeat(2.0 ** ea, 128, axis=1)
+    w64 = dec[cw] * np.repeat(2.0 ** ew, 128, axis=1)[np.arange(N) // 128]
+    A = synth.bf16_bits(a64.astype(np.float32))
+    W = synth.bf16_bits(w64.astype(np.float32))
+    aq, sa = oracle.act_quant(A)
+    wq, sw = oracle.weight_quant(W)
+    assert np.array_equal(sa, np.float32(2.0 ** ea)) and np.array_equal(sw, np.float32(2.0 ** ew))
+    y, _ = oracle.block_gemm(aq, sa, wq, sw)
+    assert np.array_equal(y, a64 @ w64.T)
+
+
+@pytest.mark.parametrize("k", [-7, 3])
+def test_gemm_power_of_two_scale_linearity(oracle_lib, k):
+    A = synth.random_bf16((16, 384), 13)
+    W = synth.random_bf16((130, 384), 14, std=0.02)
+    aq, sa = oracle.act_quant(A)
+    wq, sw = oracle.weight_quant(W)
+    y1, b1 = oracle.block_gemm(aq, sa, wq, sw)
+    y2, b2 = oracle.block_gemm(aq, np.float32(sa * np.float32(2.0 ** k)), wq, sw)
+    assert np.array_equal(y2, y1 * 2.0 ** k) and np.array_equal(b2, b1 * 2.0 ** k)
+
+
+def test_gemm_single_slice_closed_form(oracle_lib):
+    A = synth.random_bf16((7, 128), 15)
+    W = synth.random_bf16((9, 128), 16, std=0.02)
+    aq, sa = oracle.act_quant(A)
+    wq, sw = oracle.weight_quant(W)
+    y, _ = oracle.block_gemm(aq, sa, wq, sw)
+    dec = oracle.e4m3_decode_all()
+    p = dec[aq] @ dec[wq].T                       # exact: multiples of 2^-18, < 2^53
+    want = p * (sa[:, 0].astype(np.float64)[:, None] * np.float64(sw[0, 0]))
+    assert np.array_equal(y, want)
+
+
+def test_matmul_bf16_sampled(oracle_lib):
+    A = synth.random_bf16((10, 256), 17)
+    W = synth.random_bf16((20, 256), 18)
+    r, c = np.arange(10).repeat(20), np.tile(np.arange(20), 10)
+    y = oracle.matmul_bf16_sampled(A, W, r, c)
+    want = oracle.bf16_to_f32_array(A).astype(np.float64) @ oracle.bf16_to_f32_array(W).astype(np.float64).T
+    assert np.allclose(y, want.reshape(-1), rtol=1e-13, atol=1e-13)
