@@ -1,0 +1,222 @@
+#!/usr/bin/env python3
+"""Throughput of the FP8 block-scaled path on one MI355X.
+
+One step = fp8_act_quant(A) -> fp8_block_gemm(Aq, sa, Wq, sw) -> Y on the query
+down-projection workload (A 4096x7168 bf16 tokens, W 1536x7168 pre-quantised to E4M3
+128x128 blocks, Y bf16). Weights are quantised once before timing (offline, as stored
+FP8 weights are). Inputs are resident in HBM; A is rotated over several copies so that
+act_quant reads HBM rather than the 256 MB last-level cache.
+
+Prints ONE JSON line. `value` = 2*M*N*K / (time per step) in TFLOP/s, i.e. GEMM flops
+per second including the activation quantisation. `roofline` is for the dominant
+kernel (the GEMM) with its duration measured by HIP events around each launch on the
+stream it runs on; act_quant's HBM figures are reported beside it. `cpu_baseline`
+times the CPU oracle (as it is) on a bounded row sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+FP8_PEAK_TFLOPS = 5000.0      # MI355X dense FP8 MFMA
+HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
+METRIC = "fp8_block_gemm TFLOP/s (incl. act_quant) and % of MI355X FP8 MFMA peak"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_q_down_traffic.json")
+GEMM_SOURCES = ["fp8_act_quant_amd/csrc/gemm.hip", "fp8_act_quant_amd/csrc/device_common.h"]
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for p in GEMM_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per GEMM launch from the committed counter summary, if it was taken on
+    the current kernel source; otherwise None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(A, W, rows: int):
+    """The oracle on the first `rows` tokens: act_quant of those rows, then the float64
+    block GEMM (with its error bound) for all N outputs of each row."""
+    import numpy as np
+
+    import oracle
+    oracle.build(force=False)
+    M, K = A.shape
+    N = W.shape[0]
+    wq, sw = oracle.weight_quant(W)           # offline step, untimed like on the GPU
+    t0 = time.perf_counter()
+    aq, sa = oracle.act_quant(np.ascontiguousarray(A[:rows]))
+    t1 = time.perf_counter()
+    y, _ = oracle.block_gemm(aq, sa, wq, sw)
+    t2 = time.perf_counter()
+    flops = 2.0 * rows * N * K
+    return {
+        "value": flops / (t2 - t0) / 1e12,
+        "unit": "TFLOP/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"first {rows} of {M} tokens: act_quant {rows}x{K} + float64 block GEMM {rows}x{N}x{K} "
+                  f"(act_quant {t1 - t0:.2f}s, gemm {t2 - t1:.2f}s wall)",
+    }, (aq, sa, y)
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--copies", type=int, default=10, help="rotated copies of A")
+    ap.add_argument("--cpu-rows", type=int, default=2048, help="token rows in the CPU-baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the path is data-parallel over tokens with no exchange, "
+              "and this build runs on a single MI355X; --gpus must be 1.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import fp8_act_quant_amd as fq
+    import synth
+    from fp8_act_quant_amd import _lib as L
+
+    wl = synth.WORKLOADS[synth.HEADLINE]
+    M, N, K = wl.M, wl.N, wl.K
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    A_host, W_host = synth.make_inputs(wl)
+
+    a0 = torch.from_numpy(A_host.view(np.int16)).view(torch.bfloat16).to(dev)
+    copies = [a0] + [a0.clone() for _ in range(args.copies - 1)]
+    w = torch.from_numpy(W_host.view(np.int16)).view(torch.bfloat16).to(dev)
+    wq, sw = fq.weight_quant(w)
+    del w
+    aq = torch.empty((M, K), dtype=torch.float8_e4m3fn, device=dev)
+    sa = torch.empty((M, K // 128), dtype=torch.float32, device=dev)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sptr = stream.cuda_stream
+    out_code = L.FP8Q_OUT_BF16
+    ws_bytes = fq.gemm_workspace_bytes(M, N, K, torch.bfloat16)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    lib = fq.lib
+    p_aq, p_sa, p_wq, p_sw, p_y, p_ws = aq.data_ptr(), sa.data_ptr(), wq.data_ptr(), sw.data_ptr(), \
+        y.data_ptr(), ws.data_ptr()
+    xs = [c.data_ptr() for c in copies]
+
+    def step(i, ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        L.check("fp8_act_quant", lib.fp8_act_quant(xs[i % len(xs)], p_aq, p_sa, M, K, sptr))
+        if ev is not None:
+            ev[1].record(stream)
+        L.check("fp8_block_gemm", lib.fp8_block_gemm(p_aq, p_sa, p_wq, p_sw, p_y, out_code, M, N, K,
+                                                     p_ws, ws_bytes, sptr))
+        if ev is not None:
+            ev[2].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # timed region 1: back-to-back steps, whole-step throughput
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(i)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_total = t_start.elapsed_time(t_end)
+    ms_per_step = ms_total / args.steps
+
+    # timed region 2: the same steps with an event around each launch (per-kernel durations)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    t_aq = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e-3
+    t_gemm = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e-3
+
+    flops = 2.0 * M * N * K
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    gemm_tflops = flops / t_gemm.mean() / 1e12
+    aq_bytes = M * K * 2 + M * K + M * (K // 128) * 4
+    aq_gbs = aq_bytes / t_aq.mean() / 1e9
+    traffic = measured_traffic()
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3 (fp32 accumulate)",
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name}: {wl.description}", "M": M, "N": N, "K": K, "out": wl.out_dtype,
+                   "a_copies_rotated": args.copies, "weights": "pre-quantised E4M3 128x128 blocks (untimed)"},
+        "pct_of_fp8_peak": round(100.0 * value / FP8_PEAK_TFLOPS, 2),
+        "roofline": {
+            "kernel": "block_gemm_kernel",
+            "bound": "mfma",
+            "achieved": round(gemm_tflops, 2),
+            "peak": FP8_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(gemm_tflops / FP8_PEAK_TFLOPS, 4),
+            "traffic": traffic,
+            "avg_launch_us": round(float(t_gemm.mean()) * 1e6, 3),
+            "algorithmic_flops_per_launch": flops,
+        },
+        "act_quant": {
+            "kernel": "act_quant_kernel",
+            "bound": "hbm",
+            "achieved": round(aq_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(aq_gbs / HBM_PEAK_GBS, 4),
+            "avg_launch_us": round(float(t_aq.mean()) * 1e6, 3),
+            "algorithmic_bytes_per_launch": aq_bytes,
+        },
+        "gemm_only_tflops": round(gemm_tflops, 2),
+    }
+
+    if not args.no_cpu_baseline:
+        cb, (oaq, osa, oy) = cpu_baseline(A_host, W_host, args.cpu_rows)
+        # sanity: the GPU path on the same rows agrees with the oracle (codes exactly)
+        r = args.cpu_rows
+        same_codes = bool(np.array_equal(aq[:r].view(torch.uint8).cpu().numpy(), oaq))
+        cb["gpu_codes_match_oracle_on_sample"] = same_codes
+        result["cpu_baseline"] = cb
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

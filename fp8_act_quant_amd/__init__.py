@@ -1,0 +1,155 @@
+"""FP8 (E4M3) fine-grained block quantisation and block-scaled GEMM for AMD MI355X.
+
+Python names follow the linear() listing on the pomoai.com "DeepSeek-V3" page (FP8
+mixed-precision training section): ``act_quant(x, block_size) -> (x_fp8, scale)``,
+``fp8_gemm(x, scale, weight, weight_scale) -> y`` and ``weight_dequant(weight,
+weight_scale)``, plus the weight quantiser that produces the 128x128-block format.
+
+This module only marshals arguments: it checks dtypes, shapes and devices, allocates
+the outputs with torch and calls the C ABI of libfp8q.so on torch's current HIP
+stream. Every arithmetic step runs in the gfx950 kernels behind that library.
+"""
+from __future__ import annotations
+
+import math
+
+import torch
+
+from . import _lib
+from ._lib import (FP8Q_GEMM_EXACT_SLICES, FP8Q_GEMM_FP8_PRODUCTS, FP8Q_OUT_BF16, FP8Q_OUT_F32, Fp8qError,
+                   check, lib)
+
+BLOCK = 128
+
+__all__ = [
+    "BLOCK", "Fp8qError", "act_quant", "weight_quant", "weight_dequant", "fp8_gemm",
+    "gemm_workspace_bytes", "lib",
+]
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _need(t: torch.Tensor, name: str, dtype, align: int = 16) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() and t.data_ptr() % align:
+        raise ValueError(f"{name} must be {align}-byte aligned")
+
+
+def act_quant(x: torch.Tensor, block_size: int = BLOCK):
+    """Per-token, per-128-channel quantisation of a bf16 activation [..., K].
+
+    Returns ``(q, s)``: q float8_e4m3fn [..., K], s float32 [..., K/128]."""
+    if block_size != BLOCK:
+        raise ValueError("only block_size=128 is supported")
+    _need(x, "x", torch.bfloat16)
+    K = x.shape[-1]
+    if K % BLOCK:
+        raise ValueError("the last dimension must be a multiple of 128")
+    M = math.prod(x.shape[:-1])
+    q = torch.empty(x.shape, dtype=torch.float8_e4m3fn, device=x.device)
+    s = torch.empty((*x.shape[:-1], K // BLOCK), dtype=torch.float32, device=x.device)
+    with torch.cuda.device(x.device):
+        check("fp8_act_quant", lib.fp8_act_quant(x.data_ptr(), q.data_ptr(), s.data_ptr(), M, K,
+                                                 _stream(x)))
+    return q, s
+
+
+def weight_quant(w: torch.Tensor):
+    """128x128 block quantisation of a bf16 weight [N, K].
+
+    Returns ``(q, s)``: q float8_e4m3fn [N, K], s float32 [ceil(N/128), K/128]."""
+    _need(w, "w", torch.bfloat16)
+    if w.dim() != 2:
+        raise ValueError("w must be 2-D [N, K]")
+    N, K = w.shape
+    if K % BLOCK:
+        raise ValueError("K must be a multiple of 128")
+    q = torch.empty((N, K), dtype=torch.float8_e4m3fn, device=w.device)
+    s = torch.empty(((N + BLOCK - 1) // BLOCK, K // BLOCK), dtype=torch.float32, device=w.device)
+    with torch.cuda.device(w.device):
+        check("fp8_weight_quant", lib.fp8_weight_quant(w.data_ptr(), q.data_ptr(), s.data_ptr(), N, K,
+                                                       _stream(w)))
+    return q, s
+
+
+def weight_dequant(q: torch.Tensor, s: torch.Tensor) -> torch.Tensor:
+    """bf16 weight [N, K] from its E4M3 codes and 128x128 block scales."""
+    _need(q, "q", torch.float8_e4m3fn)
+    _need(s, "s", torch.float32, align=4)
+    if q.dim() != 2:
+        raise ValueError("q must be 2-D [N, K]")
+    N, K = q.shape
+    if K % BLOCK:
+        raise ValueError("K must be a multiple of 128")
+    if tuple(s.shape) != ((N + BLOCK - 1) // BLOCK, K // BLOCK):
+        raise ValueError(f"s must be [{(N + BLOCK - 1) // BLOCK}, {K // BLOCK}]")
+    w = torch.empty((N, K), dtype=torch.bfloat16, device=q.device)
+    with torch.cuda.device(q.device):
+        check("fp8_weight_dequant", lib.fp8_weight_dequant(q.data_ptr(), s.data_ptr(), w.data_ptr(), N, K,
+                                                           _stream(q)))
+    return w
+
+
+def gemm_workspace_bytes(M: int, N: int, K: int, out_dtype=torch.bfloat16) -> int:
+    code = FP8Q_OUT_BF16 if out_dtype == torch.bfloat16 else FP8Q_OUT_F32
+    return int(lib.fp8_block_gemm_workspace_bytes(M, N, K, code))
+
+
+_MODES = {"default": 0, "fp8": FP8Q_GEMM_FP8_PRODUCTS, "exact": FP8Q_GEMM_EXACT_SLICES}
+
+
+def fp8_gemm(a: torch.Tensor, a_s: torch.Tensor, w: torch.Tensor, w_s: torch.Tensor,
+             out_dtype=torch.bfloat16, workspace: torch.Tensor | None = None,
+             out: torch.Tensor | None = None, mode: str = "default") -> torch.Tensor:
+    """Block-scaled Y = A . W^T. a: float8_e4m3fn [..., K] with scales [..., K/128];
+    w: float8_e4m3fn [N, K] with scales [ceil(N/128), K/128]. Returns [..., N] in
+    out_dtype (torch.float32 or torch.bfloat16).
+
+    mode: "fp8" forms every 128-wide slice partial on the FP8 matrix unit, "exact" on the
+    f16 matrix unit from exactly converted operands; "default" is "exact" for float32
+    output and "fp8" for bfloat16 output."""
+    if mode not in _MODES:
+        raise ValueError(f"mode must be one of {sorted(_MODES)}")
+    _need(a, "a", torch.float8_e4m3fn)
+    _need(w, "w", torch.float8_e4m3fn)
+    _need(a_s, "a_s", torch.float32, align=4)
+    _need(w_s, "w_s", torch.float32, align=4)
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("out_dtype must be torch.float32 or torch.bfloat16")
+    K = a.shape[-1]
+    if w.dim() != 2 or w.shape[1] != K:
+        raise ValueError("w must be [N, K] with the activation's K")
+    if K % BLOCK:
+        raise ValueError("K must be a multiple of 128")
+    N = w.shape[0]
+    M = math.prod(a.shape[:-1])
+    if tuple(a_s.shape) != (*a.shape[:-1], K // BLOCK):
+        raise ValueError("a_s must be [..., K/128]")
+    if tuple(w_s.shape) != ((N + BLOCK - 1) // BLOCK, K // BLOCK):
+        raise ValueError("w_s must be [ceil(N/128), K/128]")
+    shape = (*a.shape[:-1], N)
+    if out is None:
+        out = torch.empty(shape, dtype=out_dtype, device=a.device)
+    else:
+        _need(out, "out", out_dtype)
+        if tuple(out.shape) != shape:
+            raise ValueError(f"out must be {shape}")
+    ws_ptr, ws_bytes = 0, 0
+    if workspace is not None:
+        _need(workspace, "workspace", workspace.dtype)
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    code = (FP8Q_OUT_BF16 if out_dtype == torch.bfloat16 else FP8Q_OUT_F32) | _MODES[mode]
+    with torch.cuda.device(a.device):
+        check("fp8_block_gemm", lib.fp8_block_gemm(a.data_ptr(), a_s.data_ptr(), w.data_ptr(), w_s.data_ptr(),
+                                                   out.data_ptr(), code, M, N, K, ws_ptr or None, ws_bytes,
+                                                   _stream(a)))
+    return out

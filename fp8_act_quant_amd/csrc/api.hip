@@ -1,0 +1,126 @@
+// api.hip -- the C ABI declared in include/fp8q.h: host-side validation, then one launch
+// on the caller's stream. Nothing here allocates, synchronises or keeps state beyond a
+// per-device "is this a gfx950" cache.
+#include <fp8q.h>
+
+#include <atomic>
+#include <cstring>
+
+#include "launch.h"
+
+namespace {
+
+constexpr int64_t kBlock = 128;
+constexpr int kMaxDevices = 64;
+// launch-geometry limits of the kernels (grid dimensions are 32-bit)
+constexpr int64_t kMaxElems = (int64_t)1 << 46;
+constexpr int64_t kMaxWeightBlockRows = 65535;
+
+bool misaligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
+
+// 0 = unknown, 1 = gfx950, 2 = other / unusable
+std::atomic<int> g_dev_kind[kMaxDevices];
+
+int check_device() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return FP8Q_ERR_UNSUPPORTED;
+    if (dev < 0 || dev >= kMaxDevices) return FP8Q_ERR_UNSUPPORTED;
+    int kind = g_dev_kind[dev].load(std::memory_order_relaxed);
+    if (kind == 0) {
+        hipDeviceProp_t prop;
+        kind = 2;
+        if (hipGetDeviceProperties(&prop, dev) == hipSuccess && std::strncmp(prop.gcnArchName, "gfx950", 6) == 0)
+            kind = 1;
+        g_dev_kind[dev].store(kind, std::memory_order_relaxed);
+    }
+    return kind == 1 ? FP8Q_OK : FP8Q_ERR_UNSUPPORTED;
+}
+
+int shape_ok(int64_t rows, int64_t K) {
+    if (rows < 0 || K < 0 || (K % kBlock) != 0) return FP8Q_ERR_SHAPE;
+    if (K > 0 && rows > kMaxElems / K) return FP8Q_ERR_SHAPE;
+    return FP8Q_OK;
+}
+
+int finish(hipError_t e) { return e == hipSuccess ? FP8Q_OK : FP8Q_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+int fp8_act_quant(const uint16_t *x, uint8_t *q, float *s, int64_t M, int64_t K, void *stream) {
+    if (int e = shape_ok(M, K)) return e;
+    if (M == 0 || K == 0) return FP8Q_OK;
+    if (!x || !q || !s) return FP8Q_ERR_NULL;
+    if (misaligned(x, 16) || misaligned(q, 16) || misaligned(s, 4)) return FP8Q_ERR_ALIGN;
+    if (int e = check_device()) return e;
+    return finish(fp8q::launch_act_quant(x, q, s, M, K, static_cast<hipStream_t>(stream)));
+}
+
+int fp8_weight_quant(const uint16_t *w, uint8_t *q, float *s, int64_t N, int64_t K, void *stream) {
+    if (int e = shape_ok(N, K)) return e;
+    if ((N + kBlock - 1) / kBlock > kMaxWeightBlockRows) return FP8Q_ERR_SHAPE;
+    if (N == 0 || K == 0) return FP8Q_OK;
+    if (!w || !q || !s) return FP8Q_ERR_NULL;
+    if (misaligned(w, 16) || misaligned(q, 16) || misaligned(s, 4)) return FP8Q_ERR_ALIGN;
+    if (int e = check_device()) return e;
+    return finish(fp8q::launch_weight_quant(w, q, s, N, K, static_cast<hipStream_t>(stream)));
+}
+
+int fp8_weight_dequant(const uint8_t *q, const float *s, uint16_t *w, int64_t N, int64_t K, void *stream) {
+    if (int e = shape_ok(N, K)) return e;
+    if (N == 0 || K == 0) return FP8Q_OK;
+    if (!w || !q || !s) return FP8Q_ERR_NULL;
+    if (misaligned(w, 16) || misaligned(q, 16) || misaligned(s, 4)) return FP8Q_ERR_ALIGN;
+    if (int e = check_device()) return e;
+    return finish(fp8q::launch_weight_dequant(q, s, w, N, K, static_cast<hipStream_t>(stream)));
+}
+
+int fp8_block_gemm(const uint8_t *aq, const float *sa, const uint8_t *wq, const float *sw, void *y,
+                   int y_dtype, int64_t M, int64_t N, int64_t K, void *workspace, size_t workspace_bytes,
+                   void *stream) {
+    const int dtype = y_dtype & 0xFF;
+    const int mode = y_dtype & ~0xFF;
+    if (dtype != FP8Q_OUT_F32 && dtype != FP8Q_OUT_BF16) return FP8Q_ERR_DTYPE;
+    if (mode != 0 && mode != FP8Q_GEMM_FP8_PRODUCTS && mode != FP8Q_GEMM_EXACT_SLICES) return FP8Q_ERR_DTYPE;
+    if (int e = shape_ok(M, K)) return e;
+    if (int e = shape_ok(N, K)) return e;
+    if (M > 0 && N > kMaxElems / M) return FP8Q_ERR_SHAPE;
+    if (M == 0 || N == 0) return FP8Q_OK;
+    if (!y) return FP8Q_ERR_NULL;
+    if (K > 0 && (!aq || !sa || !wq || !sw)) return FP8Q_ERR_NULL;
+    if (misaligned(aq, 16) || misaligned(wq, 16) || misaligned(y, 16) || misaligned(sa, 4) ||
+        misaligned(sw, 4))
+        return FP8Q_ERR_ALIGN;
+    if (workspace == nullptr) workspace_bytes = 0;
+    if (workspace_bytes && misaligned(workspace, 16)) return FP8Q_ERR_ALIGN;
+    if (int e = check_device()) return e;
+    // default contraction: exact slices for fp32 output, the FP8 matrix unit for bf16 output
+    const bool exact = mode == FP8Q_GEMM_EXACT_SLICES || (mode == 0 && dtype == FP8Q_OUT_F32);
+    return finish(fp8q::launch_block_gemm(aq, sa, wq, sw, y, dtype == FP8Q_OUT_BF16, exact, M, N, K, workspace,
+                                          workspace_bytes, static_cast<hipStream_t>(stream)));
+}
+
+size_t fp8_block_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int y_dtype) {
+    if (M <= 0 || N <= 0 || K <= 0 || (K % kBlock) != 0) return 0;
+    const int dtype = y_dtype & 0xFF;
+    if (dtype != FP8Q_OUT_F32 && dtype != FP8Q_OUT_BF16) return 0;
+    return fp8q::gemm_workspace_bytes(M, N, K, dtype == FP8Q_OUT_BF16);
+}
+
+const char *fp8q_strerror(int status) {
+    switch (status) {
+    case FP8Q_OK: return "ok";
+    case FP8Q_ERR_NULL: return "a required pointer is NULL";
+    case FP8Q_ERR_SHAPE: return "invalid shape (negative size, K not a multiple of 128, or too large)";
+    case FP8Q_ERR_ALIGN: return "pointer alignment below what the entry point requires";
+    case FP8Q_ERR_DTYPE: return "unknown output dtype";
+    case FP8Q_ERR_UNSUPPORTED: return "no gfx950 device is current";
+    case FP8Q_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+    }
+}
+
+int fp8q_version(void) { return (1 << 16) | 0; }
+
+}  // extern "C"

@@ -1,0 +1,27 @@
+// launch.h -- internal host-side launchers behind the C ABI (include/fp8q.h).
+// They assume validated arguments and enqueue on `stream`; they return the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fp8q {
+
+hipError_t launch_act_quant(const uint16_t *x, uint8_t *q, float *s, int64_t M, int64_t K,
+                            hipStream_t stream);
+hipError_t launch_weight_quant(const uint16_t *w, uint8_t *q, float *s, int64_t N, int64_t K,
+                               hipStream_t stream);
+hipError_t launch_weight_dequant(const uint8_t *q, const float *s, uint16_t *w, int64_t N, int64_t K,
+                                 hipStream_t stream);
+
+// Block-scaled GEMM. out_bf16 selects the output dtype; exact selects the exact-slice
+// contraction (f16 matrix unit on exactly converted operands) instead of the FP8 matrix
+// unit. The workspace (may be NULL) is used for a split-K schedule when workspace_bytes >=
+// gemm_workspace_bytes(M, N, K, out_bf16).
+hipError_t launch_block_gemm(const uint8_t *aq, const float *sa, const uint8_t *wq, const float *sw,
+                             void *y, bool out_bf16, bool exact, int64_t M, int64_t N, int64_t K,
+                             void *workspace, size_t workspace_bytes, hipStream_t stream);
+size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, bool out_bf16);
+
+}  // namespace fp8q

@@ -1,0 +1,170 @@
+// quant.hip -- E4M3 quantisation / dequantisation kernels for gfx950.
+//
+// act_quant: per token per 128 channels (pomoai.com "DeepSeek-V3", FP8 mixed-precision
+// training section: dynamic activation quantisation per token per 128 channels).
+// weight_quant / weight_dequant: 128x128 blocks with one fp32 scale each (same section:
+// FP8 weights in 128x128 blocks with a float32 weight_scale_inv per block).
+#include "device_common.h"
+#include "launch.h"
+
+namespace fp8q {
+
+// ------------------------------------------------------------------------------------
+// act_quant
+// A row-major [M, K] activation with K % 128 == 0 is a flat sequence of 1x128 tiles,
+// and tile t's scale is s[t] (the [M, K/128] scale grid in row-major order). One DPP row
+// (16 lanes) owns a tile: lane j holds bf16 elements 8j..8j+7 (one 16-byte load) and
+// writes their 8 codes (one 8-byte store). A wave covers 4 consecutive tiles per load
+// instruction (1 KiB contiguous) and AQ_UNROLL such groups, all loads issued before any
+// arithmetic so that AQ_UNROLL x 16 bytes per lane are in flight.
+// ------------------------------------------------------------------------------------
+constexpr int AQ_THREADS = 256;
+constexpr int AQ_UNROLL = 4;
+constexpr int AQ_TILES_PER_WAVE = 4 * AQ_UNROLL;
+constexpr int AQ_TILES_PER_BLOCK = AQ_TILES_PER_WAVE * (AQ_THREADS / 64);
+
+__global__ __launch_bounds__(AQ_THREADS) void act_quant_kernel(const u32x4 *__restrict__ x,
+                                                               u32x2 *__restrict__ q,
+                                                               float *__restrict__ s,
+                                                               int64_t n_tiles) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int64_t tile0 = (int64_t)blockIdx.x * AQ_TILES_PER_BLOCK + wave * AQ_TILES_PER_WAVE + (lane >> 4);
+    const int j = lane & 15;
+
+    u32x4 v[AQ_UNROLL];
+#pragma unroll
+    for (int u = 0; u < AQ_UNROLL; ++u) {
+        int64_t t = tile0 + 4 * u;
+        v[u] = (t < n_tiles) ? __builtin_nontemporal_load(&x[t * 16 + j]) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < AQ_UNROLL; ++u) {
+        int64_t t = tile0 + 4 * u;
+        uint32_t amax = row16_max(absmax_bits8(v[u]));
+        TileScale ts = tile_scale(amax);
+        u32x2 codes = quant8(v[u], ts);
+        if (t < n_tiles) {
+            __builtin_nontemporal_store(codes, &q[t * 16 + j]);
+            if (j == 0) s[t] = ts.s;
+        }
+    }
+}
+
+hipError_t launch_act_quant(const uint16_t *x, uint8_t *q, float *s, int64_t M, int64_t K,
+                            hipStream_t stream) {
+    const int64_t n_tiles = M * (K / kBlock);
+    if (n_tiles == 0) return hipSuccess;
+    const int64_t blocks = (n_tiles + AQ_TILES_PER_BLOCK - 1) / AQ_TILES_PER_BLOCK;
+    hipLaunchKernelGGL(act_quant_kernel, dim3((unsigned)blocks), dim3(AQ_THREADS), 0, stream,
+                       reinterpret_cast<const u32x4 *>(x), reinterpret_cast<u32x2 *>(q), s, n_tiles);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------
+// weight_quant: one workgroup (256 threads) per 128x128 block. Thread t covers the
+// 16-byte chunk (t & 15) of rows (t >> 4) + 16 i, i = 0..7. Rows past N (ragged last
+// block row) are neither read nor written and do not enter the block's amax.
+// ------------------------------------------------------------------------------------
+constexpr int WQ_THREADS = 256;
+
+__global__ __launch_bounds__(WQ_THREADS) void weight_quant_kernel(const uint16_t *__restrict__ w,
+                                                                  uint8_t *__restrict__ q,
+                                                                  float *__restrict__ s,
+                                                                  int64_t N, int64_t K) {
+    __shared__ uint32_t wave_max[WQ_THREADS / 64];
+    const int64_t kb = blockIdx.x, nb = blockIdx.y;
+    const int64_t nkb = K / kBlock;
+    const int t = threadIdx.x;
+    const int chunk = t & 15;
+    const int64_t row0 = nb * kBlock + (t >> 4);
+
+    u32x4 v[8];
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        int64_t r = row0 + 16 * i;
+        v[i] = (r < N) ? *reinterpret_cast<const u32x4 *>(w + r * K + kb * kBlock + chunk * 8)
+                       : u32x4{0, 0, 0, 0};
+        uint32_t a = absmax_bits8(v[i]);
+        m = m > a ? m : a;
+    }
+    m = row16_max(m);
+    // combine the four DPP rows of the wave, then the four waves
+    uint32_t r0 = __builtin_amdgcn_readlane(m, 0), r1 = __builtin_amdgcn_readlane(m, 16);
+    uint32_t r2 = __builtin_amdgcn_readlane(m, 32), r3 = __builtin_amdgcn_readlane(m, 48);
+    r0 = r0 > r1 ? r0 : r1;
+    r2 = r2 > r3 ? r2 : r3;
+    if ((t & 63) == 0) wave_max[t >> 6] = r0 > r2 ? r0 : r2;
+    __syncthreads();
+    uint32_t amax = wave_max[0];
+#pragma unroll
+    for (int i = 1; i < WQ_THREADS / 64; ++i) amax = amax > wave_max[i] ? amax : wave_max[i];
+
+    TileScale ts = tile_scale(amax);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        int64_t r = row0 + 16 * i;
+        u32x2 codes = quant8(v[i], ts);
+        if (r < N) *reinterpret_cast<u32x2 *>(q + r * K + kb * kBlock + chunk * 8) = codes;
+    }
+    if (t == 0) s[nb * nkb + kb] = ts.s;
+}
+
+hipError_t launch_weight_quant(const uint16_t *w, uint8_t *q, float *s, int64_t N, int64_t K,
+                               hipStream_t stream) {
+    const int64_t nkb = K / kBlock, nnb = (N + kBlock - 1) / kBlock;
+    if (nkb == 0 || nnb == 0) return hipSuccess;
+    hipLaunchKernelGGL(weight_quant_kernel, dim3((unsigned)nkb, (unsigned)nnb), dim3(WQ_THREADS), 0,
+                       stream, w, q, s, N, K);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------
+// weight_dequant: each thread turns one 16-byte chunk of codes (16 consecutive k inside
+// one 128-wide block) into 16 bf16 values: decode (v_cvt_pk_f32_fp8), one fp32 multiply
+// by the block scale, round to bf16 (v_cvt_pk_bf16_f32).
+// ------------------------------------------------------------------------------------
+constexpr int DQ_THREADS = 256;
+
+template <bool HI>
+__device__ __forceinline__ uint32_t dequant_pair(uint32_t word, float sc) {
+    f32x2_t f = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, HI);
+    return pack_bf16x2(f[0] * sc, f[1] * sc);
+}
+
+__global__ __launch_bounds__(DQ_THREADS) void weight_dequant_kernel(const u32x4 *__restrict__ q,
+                                                                    const float *__restrict__ s,
+                                                                    u32x4 *__restrict__ w,
+                                                                    int64_t n_chunks, int64_t K) {
+    const int64_t c = (int64_t)blockIdx.x * DQ_THREADS + threadIdx.x;
+    if (c >= n_chunks) return;
+    const int64_t chunks_per_row = K / 16;
+    const int64_t n = c / chunks_per_row;
+    const int64_t k = (c - n * chunks_per_row) * 16;
+    const float sc = s[(n / kBlock) * (K / kBlock) + k / kBlock];
+    const u32x4 v = __builtin_nontemporal_load(&q[c]);
+    u32x4 o0, o1;
+    o0.x = dequant_pair<false>(v.x, sc);
+    o0.y = dequant_pair<true>(v.x, sc);
+    o0.z = dequant_pair<false>(v.y, sc);
+    o0.w = dequant_pair<true>(v.y, sc);
+    o1.x = dequant_pair<false>(v.z, sc);
+    o1.y = dequant_pair<true>(v.z, sc);
+    o1.z = dequant_pair<false>(v.w, sc);
+    o1.w = dequant_pair<true>(v.w, sc);
+    __builtin_nontemporal_store(o0, &w[2 * c]);
+    __builtin_nontemporal_store(o1, &w[2 * c + 1]);
+}
+
+hipError_t launch_weight_dequant(const uint8_t *q, const float *s, uint16_t *w, int64_t N, int64_t K,
+                                 hipStream_t stream) {
+    const int64_t n_chunks = N * (K / 16);
+    if (n_chunks == 0) return hipSuccess;
+    const int64_t blocks = (n_chunks + DQ_THREADS - 1) / DQ_THREADS;
+    hipLaunchKernelGGL(weight_dequant_kernel, dim3((unsigned)blocks), dim3(DQ_THREADS), 0, stream,
+                       reinterpret_cast<const u32x4 *>(q), s, reinterpret_cast<u32x4 *>(w), n_chunks, K);
+    return hipGetLastError();
+}
+
+}  // namespace fp8q

@@ -61,6 +61,7 @@ def _load():
         "or_matmul_bf16_sampled": (None, [P, P, I64, P, P, I64, P]),
         "or_e4m3_encode_batch": (None, [P, P, I64]),
         "or_f32_to_bf16_batch": (None, [P, P, I64]),
+        "or_f64_to_bf16_batch": (None, [P, P, I64]),
         "or_num_threads": (ctypes.c_int, []),
         "or_set_num_threads": (None, [ctypes.c_int]),
     }
@@ -111,6 +112,14 @@ def f32_to_bf16_array(v: np.ndarray) -> np.ndarray:
     v = _c(v.astype(np.float32, copy=False), np.float32)
     out = np.empty(v.shape, dtype=np.uint16)
     _load().or_f32_to_bf16_batch(_ptr(v), _ptr(out), v.size)
+    return out
+
+
+def f64_to_bf16_array(v: np.ndarray) -> np.ndarray:
+    """Round float64 values to bf16 bit patterns (nearest, ties to even)."""
+    v = _c(v.astype(np.float64, copy=False), np.float64)
+    out = np.empty(v.shape, dtype=np.uint16)
+    _load().or_f64_to_bf16_batch(_ptr(v), _ptr(out), v.size)
     return out
 
 

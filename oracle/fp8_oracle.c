@@ -88,6 +88,35 @@ uint16_t or_f32_to_bf16(float v)
     return (lo & 1) ? hi : lo;
 }
 
+/* Round a float64 value to the nearest bf16, ties to the even pattern, by the same
+ * "nearer of the two bracketing bf16 values" rule. The lower candidate is the bf16
+ * truncation (toward zero) of the fp32 truncation of v, so |lo| <= |v| < |lo + 1|; both
+ * distances are exact in float64 (Sterbenz: the candidates lie within a factor of two
+ * of v). Used for the rounded reference of bf16 GEMM outputs. */
+uint16_t or_f64_to_bf16(double v)
+{
+    if (isnan(v))
+        return 0x7FC0;
+    float f = (float)v;
+    if (fabs((double)f) > fabs(v))
+        f = nextafterf(f, 0.0f);          /* truncate toward zero */
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    uint16_t lo = (uint16_t)(u >> 16);
+    if ((lo & 0x7FFF) >= 0x7F80)
+        return lo;                         /* |v| beyond every finite fp32: infinity */
+    if (bf16_as_double_ext(lo) == v)
+        return lo;
+    uint16_t hi = (uint16_t)(lo + 1);
+    double dlo = fabs(v - bf16_as_double_ext(lo));
+    double dhi = fabs(bf16_as_double_ext(hi) - v);
+    if (dlo < dhi)
+        return lo;
+    if (dhi < dlo)
+        return hi;
+    return (lo & 1) ? hi : lo;
+}
+
 /* OCP E4M3FN decode, closed form. Code s.eeee.mmm:
  *   e = 15 and m = 7 -> NaN;  e = 0 -> m * 2^-9 (subnormal);  else (8 + m) * 2^(e - 10),
  * i.e. (1 + m/8) * 2^(e - 7) with exponent bias 7; the sign is applied last. */
@@ -314,6 +343,13 @@ void or_f32_to_bf16_batch(const float *v, uint16_t *out, int64_t n)
 #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < n; ++i)
         out[i] = or_f32_to_bf16(v[i]);
+}
+
+void or_f64_to_bf16_batch(const double *v, uint16_t *out, int64_t n)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = or_f64_to_bf16(v[i]);
 }
 
 int or_num_threads(void)

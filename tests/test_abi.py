@@ -1,0 +1,135 @@
+"""The C ABI library (no GPU needed): it loads, exports every function include/fp8q.h
+declares, and rejects invalid arguments on the host before touching a device."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8q.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?(?:int|size_t|char)\s*\*?\s*(\w+)\s*\(", src, flags=re.M)
+
+
+def test_header_declares_the_boundary():
+    names = set(_declared())
+    assert {"fp8_act_quant", "fp8_weight_quant", "fp8_weight_dequant", "fp8_block_gemm",
+            "fp8_block_gemm_workspace_bytes", "fp8q_strerror", "fp8q_version"} <= names
+
+
+def test_library_exports_every_declared_symbol():
+    from fp8_act_quant_amd import _lib
+    lib = ctypes.CDLL(_lib.LIB_PATH)
+    for name in _declared():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    assert set(_declared()) <= exported
+    assert set(_lib.SIGNATURES) == set(_declared())
+
+
+def test_binding_has_no_cpu_fallback():
+    import fp8_act_quant_amd as fq
+    src = open(os.path.join(ROOT, "fp8_act_quant_amd", "__init__.py")).read()
+    assert "oracle" not in src
+    assert fq.lib._name.endswith("libfp8q.so")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from fp8_act_quant_amd import _lib
+    return _lib.lib
+
+
+FAKE = 0x10000  # never dereferenced: every call below fails validation first
+
+
+def test_strerror_and_version(lib):
+    from fp8_act_quant_amd import _lib
+    for code in range(0, 7):
+        assert lib.fp8q_strerror(code)
+    assert lib.fp8q_strerror(99) == b"unknown status"
+    assert lib.fp8q_version() >> 16 == 1
+    assert _lib.strerror(_lib.FP8Q_ERR_ALIGN).startswith("pointer alignment")
+
+
+def test_act_quant_validation(lib):
+    from fp8_act_quant_amd import _lib as L
+    assert lib.fp8_act_quant(FAKE, FAKE, FAKE, 4, 100, None) == L.FP8Q_ERR_SHAPE
+    assert lib.fp8_act_quant(FAKE, FAKE, FAKE, -1, 128, None) == L.FP8Q_ERR_SHAPE
+    assert lib.fp8_act_quant(FAKE, FAKE, FAKE, 4, -128, None) == L.FP8Q_ERR_SHAPE
+    assert lib.fp8_act_quant(None, FAKE, FAKE, 4, 128, None) == L.FP8Q_ERR_NULL
+    assert lib.fp8_act_quant(FAKE, None, FAKE, 4, 128, None) == L.FP8Q_ERR_NULL
+    assert lib.fp8_act_quant(FAKE, FAKE, None, 4, 128, None) == L.FP8Q_ERR_NULL
+    assert lib.fp8_act_quant(FAKE + 8, FAKE, FAKE, 4, 128, None) == L.FP8Q_ERR_ALIGN
+    assert lib.fp8_act_quant(FAKE, FAKE + 4, FAKE, 4, 128, None) == L.FP8Q_ERR_ALIGN
+    assert lib.fp8_act_quant(FAKE, FAKE, FAKE + 2, 4, 128, None) == L.FP8Q_ERR_ALIGN
+    # empty calls are valid no-ops, even with NULL pointers
+    assert lib.fp8_act_quant(None, None, None, 0, 128, None) == L.FP8Q_OK
+    assert lib.fp8_act_quant(None, None, None, 5, 0, None) == L.FP8Q_OK
+    # sizes beyond the kernels' addressing are rejected
+    assert lib.fp8_act_quant(FAKE, FAKE, FAKE, 1 << 40, 1 << 20, None) == L.FP8Q_ERR_SHAPE
+
+
+def test_weight_quant_and_dequant_validation(lib):
+    from fp8_act_quant_amd import _lib as L
+    for fn in (lib.fp8_weight_quant,):
+        assert fn(FAKE, FAKE, FAKE, 4, 130, None) == L.FP8Q_ERR_SHAPE
+        assert fn(None, FAKE, FAKE, 4, 128, None) == L.FP8Q_ERR_NULL
+        assert fn(FAKE, FAKE + 1, FAKE, 4, 128, None) == L.FP8Q_ERR_ALIGN
+        assert fn(None, None, None, 0, 256, None) == L.FP8Q_OK
+        assert fn(FAKE, FAKE, FAKE, 128 * 65536, 128, None) == L.FP8Q_ERR_SHAPE
+    assert lib.fp8_weight_dequant(FAKE, FAKE, FAKE, 4, 64, None) == L.FP8Q_ERR_SHAPE
+    assert lib.fp8_weight_dequant(FAKE, None, FAKE, 4, 128, None) == L.FP8Q_ERR_NULL
+    assert lib.fp8_weight_dequant(FAKE, FAKE, FAKE + 2, 4, 128, None) == L.FP8Q_ERR_ALIGN
+    assert lib.fp8_weight_dequant(FAKE, FAKE + 1, FAKE, 4, 128, None) == L.FP8Q_ERR_ALIGN
+    assert lib.fp8_weight_dequant(None, None, None, 3, 0, None) == L.FP8Q_OK
+
+
+def test_block_gemm_validation(lib):
+    from fp8_act_quant_amd import _lib as L
+    g = lib.fp8_block_gemm
+    ok = dict(aq=FAKE, sa=FAKE, wq=FAKE, sw=FAKE, y=FAKE, dt=L.FP8Q_OUT_BF16, M=4, N=4, K=128)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return g(a["aq"], a["sa"], a["wq"], a["sw"], a["y"], a["dt"], a["M"], a["N"], a["K"],
+                 a.get("ws"), a.get("wsb", 0), None)
+
+    assert call(dt=7) == L.FP8Q_ERR_DTYPE
+    assert call(K=96) == L.FP8Q_ERR_SHAPE
+    assert call(M=-2) == L.FP8Q_ERR_SHAPE
+    assert call(N=-2) == L.FP8Q_ERR_SHAPE
+    assert call(y=None) == L.FP8Q_ERR_NULL
+    assert call(aq=None) == L.FP8Q_ERR_NULL
+    assert call(sw=None) == L.FP8Q_ERR_NULL
+    assert call(aq=FAKE + 8) == L.FP8Q_ERR_ALIGN
+    assert call(y=FAKE + 4) == L.FP8Q_ERR_ALIGN
+    assert call(sa=FAKE + 1) == L.FP8Q_ERR_ALIGN
+    assert call(ws=FAKE + 8, wsb=4096) == L.FP8Q_ERR_ALIGN
+    assert call(M=0, aq=None, sa=None, wq=None, sw=None, y=None) == L.FP8Q_OK
+    assert call(N=0, aq=None, sa=None, wq=None, sw=None, y=None) == L.FP8Q_OK
+    assert call(M=1 << 30, N=1 << 30) == L.FP8Q_ERR_SHAPE
+    assert lib.fp8_block_gemm_workspace_bytes(4096, 576, 7168, L.FP8Q_OUT_BF16) >= 0
+    assert lib.fp8_block_gemm_workspace_bytes(4, 4, 100, L.FP8Q_OUT_BF16) == 0
+    assert lib.fp8_block_gemm_workspace_bytes(4, 4, 128, 9) == 0
+
+
+def test_python_binding_rejects_cpu_tensors_and_bad_shapes():
+    import torch
+
+    import fp8_act_quant_amd as fq
+    with pytest.raises(ValueError):
+        fq.act_quant(torch.zeros(4, 128, dtype=torch.bfloat16))
+    with pytest.raises(ValueError):
+        fq.weight_quant(torch.zeros(4, 128, dtype=torch.bfloat16))
+    with pytest.raises(ValueError):
+        fq.act_quant(torch.zeros(4, 128, dtype=torch.bfloat16), block_size=64)

@@ -467,3 +467,24 @@ def test_matmul_bf16_sampled(oracle_lib):
     y = oracle.matmul_bf16_sampled(A, W, r, c)
     want = oracle.bf16_to_f32_array(A).astype(np.float64) @ oracle.bf16_to_f32_array(W).astype(np.float64).T
     assert np.allclose(y, want.reshape(-1), rtol=1e-13, atol=1e-13)
+
+
+def test_f64_to_bf16_single_rounding(oracle_lib):
+    # On doubles that are fp32 values, torch's float64 -> bfloat16 cast is one rounding and
+    # must agree. Just off a bf16 midpoint (+- one float64 ulp) a correct single rounding
+    # goes to the nearer neighbour (torch detours through fp32 there and lands on the
+    # midpoint, so it is not used for those); exact midpoints go to the even pattern.
+    rng = np.random.Generator(np.random.PCG64(4))
+    v = (rng.standard_normal(1 << 18) * np.exp2(rng.integers(-130, 120, size=1 << 18))).astype(np.float32)
+    v = np.concatenate([v, -v]).astype(np.float64)
+    want = torch.from_numpy(v.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(oracle.f64_to_bf16_array(v), want)
+    b = rng.integers(0, 0x7F7F, size=4096).astype(np.uint32)
+    lo = (b << 16).view(np.float32).astype(np.float64)
+    hi = ((b + 1) << 16).view(np.float32).astype(np.float64)
+    mid = (lo + hi) / 2
+    assert np.array_equal(oracle.f64_to_bf16_array(np.nextafter(mid, 0)), b.astype(np.uint16))
+    assert np.array_equal(oracle.f64_to_bf16_array(np.nextafter(mid, np.inf)), (b + 1).astype(np.uint16))
+    even = np.where((b & 1) == 0, b, b + 1).astype(np.uint16)
+    assert np.array_equal(oracle.f64_to_bf16_array(mid), even)
+    assert np.array_equal(oracle.f64_to_bf16_array(-mid), even | 0x8000)
