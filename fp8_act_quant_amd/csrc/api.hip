@@ -15,6 +15,8 @@ constexpr int kMaxDevices = 64;
 // launch-geometry limits of the kernels (grid dimensions are 32-bit)
 constexpr int64_t kMaxElems = (int64_t)1 << 46;
 constexpr int64_t kMaxWeightBlockRows = 65535;
+// the GEMM addresses a workgroup's rows of A and W with 32-bit offsets: K <= 2^24
+constexpr int64_t kMaxGemmK = (int64_t)1 << 24;
 
 bool misaligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
 
@@ -86,6 +88,7 @@ int fp8_block_gemm(const uint8_t *aq, const float *sa, const uint8_t *wq, const 
     if (int e = shape_ok(M, K)) return e;
     if (int e = shape_ok(N, K)) return e;
     if (M > 0 && N > kMaxElems / M) return FP8Q_ERR_SHAPE;
+    if (K > kMaxGemmK) return FP8Q_ERR_SHAPE;
     if (M == 0 || N == 0) return FP8Q_OK;
     if (!y) return FP8Q_ERR_NULL;
     if (K > 0 && (!aq || !sa || !wq || !sw)) return FP8Q_ERR_NULL;
