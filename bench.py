@@ -53,6 +53,52 @@ def measured_traffic():
     return t.get("hbm_bytes_per_launch")
 
 
+COPY_BYTES = 256 << 20   # bytes read (and written) by the calibration copy
+
+
+def _per_dispatch(csv_path: str, counter: str):
+    """Mean counter value per dispatch, by kernel-name prefix, from a rocprofv3 counter CSV."""
+    import csv
+    sums, counts = {}, {}
+    with open(csv_path) as f:
+        for row in csv.DictReader(f):
+            if row.get("Counter_Name") != counter:
+                continue
+            name = row["Kernel_Name"]
+            key = ("gemm" if "block_gemm_kernel" in name else "act_quant" if "act_quant_kernel" in name
+                   else "copy" if "MulFunctor" in name else None)
+            if key is None:
+                continue
+            d = (row.get("Dispatch_Id") or row.get("Correlation_Id") or str(len(sums)), key)
+            sums[d] = sums.get(d, 0.0) + float(row["Counter_Value"])
+    out = {}
+    for (_, key), v in sums.items():
+        out.setdefault(key, []).append(v)
+    return {k: sum(v) / len(v) for k, v in out.items()}
+
+
+def write_traffic_summary(fetch_csv: str, write_csv: str) -> dict:
+    """HBM bytes per GEMM (and act_quant) launch from FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch), each scaled by what the same counter reads for the calibration copy of
+    COPY_BYTES; stored with the hash of the kernel source it was taken on."""
+    fetch, write = _per_dispatch(fetch_csv, "FETCH_SIZE"), _per_dispatch(write_csv, "WRITE_SIZE")
+    f_scale = COPY_BYTES / (fetch["copy"] * 1024.0)
+    w_scale = COPY_BYTES / (write["copy"] * 1024.0)
+    summary = {
+        "kernel_source_sha": kernel_source_sha(),
+        "workload": "q_down 4096x1536x7168 bf16 out",
+        "fetch_kib_per_dispatch": {k: round(v, 1) for k, v in fetch.items()},
+        "write_kib_per_dispatch": {k: round(v, 1) for k, v in write.items()},
+        "copy_scale": {"fetch": round(f_scale, 4), "write": round(w_scale, 4), "copy_bytes": COPY_BYTES},
+        "hbm_bytes_per_launch": round(fetch["gemm"] * 1024.0 * f_scale + write["gemm"] * 1024.0 * w_scale),
+        "act_quant_hbm_bytes_per_launch": round(fetch["act_quant"] * 1024.0 * f_scale +
+                                                write["act_quant"] * 1024.0 * w_scale),
+    }
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(summary, f, indent=1)
+    return summary
+
+
 def cpu_baseline(A, W, rows: int):
     """The oracle on the first `rows` tokens: act_quant of those rows, then the float64
     block GEMM (with its error bound) for all N outputs of each row."""
@@ -87,7 +133,15 @@ def main() -> int:
     ap.add_argument("--copies", type=int, default=10, help="rotated copies of A")
     ap.add_argument("--cpu-rows", type=int, default=2048, help="token rows in the CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="after the timed steps, run a plain device copy of known size (for counter scaling)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the GEMM's HBM traffic summary from two rocprofv3 --pmc runs and exit")
     args = ap.parse_args()
+
+    if args.traffic_from:
+        print(json.dumps(write_traffic_summary(*args.traffic_from)), flush=True)
+        return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the path is data-parallel over tokens with no exchange, "
@@ -119,7 +173,7 @@ def main() -> int:
     sptr = stream.cuda_stream
     out_code = L.FP8Q_OUT_BF16
     ws_bytes = fq.gemm_workspace_bytes(M, N, K, torch.bfloat16)
-    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device=dev)   # zero-filled before first use
     lib = fq.lib
     p_aq, p_sa, p_wq, p_sw, p_y, p_ws = aq.data_ptr(), sa.data_ptr(), wq.data_ptr(), sw.data_ptr(), \
         y.data_ptr(), ws.data_ptr()
@@ -178,7 +232,7 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8_e4m3 (fp32 accumulate)",
+        "dtype": "fp8_e4m3",
         "data": "synthetic",
         "config": {"workload": f"{wl.name}: {wl.description}", "M": M, "N": N, "K": K, "out": wl.out_dtype,
                    "a_copies_rotated": args.copies, "weights": "pre-quantised E4M3 128x128 blocks (untimed)"},
@@ -211,9 +265,17 @@ def main() -> int:
         cb, (oaq, osa, oy) = cpu_baseline(A_host, W_host, args.cpu_rows)
         # sanity: the GPU path on the same rows agrees with the oracle (codes exactly)
         r = args.cpu_rows
-        same_codes = bool(np.array_equal(aq[:r].view(torch.uint8).cpu().numpy(), oaq))
-        cb["gpu_codes_match_oracle_on_sample"] = same_codes
+        gpu_codes = aq[:r].view(torch.uint8).cpu().numpy()
+        cb["gpu_codes_match_oracle_on_sample"] = bool(np.array_equal(gpu_codes, oaq))
+        cb["gpu_code_mismatches_on_sample"] = int(np.count_nonzero(gpu_codes != oaq))
         result["cpu_baseline"] = cb
+    if args.calibrate_copy:
+        # a plain streaming kernel of known size (reads and writes COPY_BYTES), untimed
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
     print(json.dumps(result), flush=True)
     return 0
 

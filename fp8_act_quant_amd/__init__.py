@@ -99,24 +99,47 @@ def weight_dequant(q: torch.Tensor, s: torch.Tensor) -> torch.Tensor:
     return w
 
 
-def gemm_workspace_bytes(M: int, N: int, K: int, out_dtype=torch.bfloat16) -> int:
-    code = FP8Q_OUT_BF16 if out_dtype == torch.bfloat16 else FP8Q_OUT_F32
-    return int(lib.fp8_block_gemm_workspace_bytes(M, N, K, code))
-
-
 _MODES = {"default": 0, "fp8": FP8Q_GEMM_FP8_PRODUCTS, "exact": FP8Q_GEMM_EXACT_SLICES}
 
 
+def _gemm_code(out_dtype, mode: str) -> int:
+    return (FP8Q_OUT_BF16 if out_dtype == torch.bfloat16 else FP8Q_OUT_F32) | _MODES[mode]
+
+
+def gemm_workspace_bytes(M: int, N: int, K: int, out_dtype=torch.bfloat16, mode: str = "default") -> int:
+    """Bytes of workspace that let fp8_gemm use its split-K schedule for this shape (0 if
+    the shape does not use one)."""
+    return int(lib.fp8_block_gemm_workspace_bytes(M, N, K, _gemm_code(out_dtype, mode)))
+
+
+# Split-K workspaces kept per (device, stream): zero-filled once, and left ready for reuse
+# by every call (the library resets its arrival counters). One per stream, because calls
+# that may overlap must not share one.
+_WORKSPACES: dict = {}
+
+
+def _auto_workspace(device: torch.device, stream: int, nbytes: int) -> torch.Tensor:
+    key = (device.index, stream)
+    ws = _WORKSPACES.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        _WORKSPACES[key] = ws
+    return ws
+
+
 def fp8_gemm(a: torch.Tensor, a_s: torch.Tensor, w: torch.Tensor, w_s: torch.Tensor,
-             out_dtype=torch.bfloat16, workspace: torch.Tensor | None = None,
-             out: torch.Tensor | None = None, mode: str = "default") -> torch.Tensor:
+             out_dtype=torch.bfloat16, workspace="auto", out: torch.Tensor | None = None,
+             mode: str = "default") -> torch.Tensor:
     """Block-scaled Y = A . W^T. a: float8_e4m3fn [..., K] with scales [..., K/128];
     w: float8_e4m3fn [N, K] with scales [ceil(N/128), K/128]. Returns [..., N] in
     out_dtype (torch.float32 or torch.bfloat16).
 
     mode: "fp8" forms every 128-wide slice partial on the FP8 matrix unit, "exact" on the
     f16 matrix unit from exactly converted operands; "default" is "exact" for float32
-    output and "fp8" for bfloat16 output."""
+    output and "fp8" for bfloat16 output.
+
+    workspace: "auto" (a zero-initialised workspace cached per device and stream), None
+    (no split-K), or a uint8 tensor that was zero-filled before its first use."""
     if mode not in _MODES:
         raise ValueError(f"mode must be one of {sorted(_MODES)}")
     _need(a, "a", torch.float8_e4m3fn)
@@ -143,11 +166,18 @@ def fp8_gemm(a: torch.Tensor, a_s: torch.Tensor, w: torch.Tensor, w_s: torch.Ten
         _need(out, "out", out_dtype)
         if tuple(out.shape) != shape:
             raise ValueError(f"out must be {shape}")
+    code = _gemm_code(out_dtype, mode)
     ws_ptr, ws_bytes = 0, 0
-    if workspace is not None:
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError('workspace must be "auto", None or a tensor')
+        need = int(lib.fp8_block_gemm_workspace_bytes(M, N, K, code)) if M and N and K else 0
+        if need:
+            ws = _auto_workspace(a.device, _stream(a), need)
+            ws_ptr, ws_bytes = ws.data_ptr(), ws.numel()
+    elif workspace is not None:
         _need(workspace, "workspace", workspace.dtype)
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
-    code = (FP8Q_OUT_BF16 if out_dtype == torch.bfloat16 else FP8Q_OUT_F32) | _MODES[mode]
     with torch.cuda.device(a.device):
         check("fp8_block_gemm", lib.fp8_block_gemm(a.data_ptr(), a_s.data_ptr(), w.data_ptr(), w_s.data_ptr(),
                                                    out.data_ptr(), code, M, N, K, ws_ptr or None, ws_bytes,

@@ -105,10 +105,14 @@ int fp8_block_gemm(const uint8_t *aq, const float *sa, const uint8_t *wq, const 
 }
 
 size_t fp8_block_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int y_dtype) {
-    if (M <= 0 || N <= 0 || K <= 0 || (K % kBlock) != 0) return 0;
+    if (M <= 0 || N <= 0 || K <= 0 || (K % kBlock) != 0 || K > kMaxGemmK) return 0;
+    if (N > kMaxElems / M || shape_ok(M, K) || shape_ok(N, K)) return 0;
     const int dtype = y_dtype & 0xFF;
+    const int mode = y_dtype & ~0xFF;
     if (dtype != FP8Q_OUT_F32 && dtype != FP8Q_OUT_BF16) return 0;
-    return fp8q::gemm_workspace_bytes(M, N, K, dtype == FP8Q_OUT_BF16);
+    if (mode != 0 && mode != FP8Q_GEMM_FP8_PRODUCTS && mode != FP8Q_GEMM_EXACT_SLICES) return 0;
+    const bool exact = mode == FP8Q_GEMM_EXACT_SLICES || (mode == 0 && dtype == FP8Q_OUT_F32);
+    return fp8q::gemm_workspace_bytes(M, N, K, dtype == FP8Q_OUT_BF16, exact);
 }
 
 const char *fp8q_strerror(int status) {

@@ -19,15 +19,31 @@
 // for one m = l % 16, so a lane needs one activation scale per 16-row group of m and its
 // four outputs are consecutive in a row of Y.
 //
-// Tiling. A 256-thread workgroup owns a BM x BN output tile; its 4 waves form a
-// WAVES_M x WAVES_N grid, each owning (16*SUB_M) x (16*SUB_N). Both operands are
-// K-contiguous. Each K slice of the tile (BM + BN rows of 128 bytes, plus the BM
-// activation scales of that slice) is copied global -> LDS by the LDS-DMA loads
-// (global_load_lds), bypassing registers, into one of NSTAGE buffers: the copies for
-// slice kb + NSTAGE - 1 are in flight while slice kb is contracted. 16-byte chunks of a row
-// are XOR-swizzled (swz_chunk) so that fragment reads are free of bank conflicts.
-// Rows past M or N are clamped to the last valid row: they only feed outputs that are
-// never stored.
+// Tiling. A workgroup of NW waves owns a BM x BN output tile (or, with split-K, one of
+// `splits` contiguous K ranges of it); its waves form a WAVES_M x WAVES_N grid, each owning
+// (16*SUB_M) x (16*SUB_N). Both operands are K-contiguous. Each K slice of the tile (BM + BN
+// rows of 128 bytes, plus the BM activation scales and the tile's weight scales of that
+// slice) is copied global -> LDS by LDS-DMA loads (buffer_load ... lds), bypassing
+// registers, into one of NSTAGE stage buffers. 16-byte chunks of a row are XOR-swizzled
+// (swz_chunk) so that fragment reads are free of bank conflicts. Rows past M or N lie
+// outside the loads' buffer range and read as zero; they only feed outputs that are never
+// stored.
+//
+// Schedule of one slice, per wave. The W fragments of the slice and the A fragment of the
+// first 16-row group are in registers when it starts. For each row group i the A
+// fragment of group i+1 is read, the SUB_N MFMAs of group i are issued, and between them
+// the promotion FMAs of group i-1 (whose MFMAs have finished by then); scheduling barriers
+// keep the compiler from regrouping these. After the last group's MFMAs are issued the
+// wave waits for its share of the next slice's copies, meets the other waves at the
+// workgroup barrier (after which the finished slice's buffer is free), queues the copies
+// of slice kb + NSTAGE into that buffer, reads the next slice's first fragments, and only
+// then promotes the last group: the matrix unit stays busy across the barrier.
+//
+// Split-K. For shapes with too few tiles to fill the 256 CUs the K slices are divided into
+// `splits` contiguous ranges. Each workgroup stores its fp32 partial tile to the caller's
+// workspace and bumps the tile's arrival counter; the last to arrive adds the partials in
+// split order (so the result does not depend on arrival order), writes Y and resets the
+// counter to zero.
 #include <cstdlib>
 #include <cstring>
 
@@ -38,25 +54,31 @@ namespace fp8q {
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int G_SLICE = 128;   // K slice = promotion interval = one f8f6f4 MFMA
 
+__device__ __forceinline__ int64_t min64(int64_t a, int64_t b) { return a < b ? a : b; }
+
 template <int BM, int BN, int NSTAGE, int NW>
 struct GemmSmem {
-    static_assert(BM % 64 == 0 && BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "tile shape");
+    static_assert(BM % 64 == 0 && BN % 64 == 0 && BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "tile shape");
     static constexpr int A_BYTES = BM * G_SLICE;
     static constexpr int W_BYTES = BN * G_SLICE;
     static constexpr int SA_BYTES = BM * 4;
-    static constexpr int SW_BYTES = 64 * 4;   // weight scales of the tile's N-blocks (<= 64)
+    static constexpr int SW_BYTES = 64 * 4;   // weight scales of 64 N-blocks from the tile's first
     static constexpr int STAGE = A_BYTES + W_BYTES + SA_BYTES + SW_BYTES;
-    static constexpr int TOTAL = STAGE * NSTAGE;
+    static constexpr int FLAG = STAGE * NSTAGE;   // split-K "last to arrive" flag
+    static constexpr int TOTAL = FLAG + 16;
     // LDS-DMA instructions per wave and slice: each tile instruction moves 1 KiB (8 rows of
     // 128 B), each scale instruction 256 B (64 rows of one fp32)
-    static constexpr int A_INSTR = BM / (8 * NW), W_INSTR = BN / (8 * NW), SA_INSTR = BM / 64;
-    static constexpr int INSTR_PER_WAVE = A_INSTR + W_INSTR + 2;
+    static constexpr int A_INSTR = BM / (8 * NW), W_INSTR = BN / (8 * NW);
+    static constexpr int SA_BLOCKS = BM / 64, SA_INSTR = (SA_BLOCKS + NW - 1) / NW;
+    static constexpr int IPW = A_INSTR + W_INSTR + SA_INSTR + 1;
+    static_assert((NSTAGE - 1) * IPW < 64, "vmcnt range");
 };
 
 // 16-byte chunk c of LDS row r is stored at physical chunk c ^ (r & 7). With the fragment
@@ -111,6 +133,15 @@ __device__ __forceinline__ i32x8 load_frag(const uint8_t *base, int row, int kgr
     return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 }
 
+// acc += p * f per element. The empty asm consumes the result where the FMAs are written:
+// without it the compiler sinks all promotions of a slice past the branches that follow
+// them, keeping every slice partial live at once (and spilling).
+__device__ __forceinline__ void promote(f32x4 &acc, const f32x4 &p, float f) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[r] = __builtin_fmaf(p[r], f, acc[r]);
+    asm volatile("" : "+v"(acc));
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
@@ -118,7 +149,32 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// Wait until the copies of a slice have landed, given that `later` slices were
+// queued after it (vector-memory loads retire in issue order, IPW instructions per slice).
+template <int IPW, int L>
+__device__ __forceinline__ void wait_slice(int later) {
+    if constexpr (L == 0) {
+        wait_vmcnt<0>();
+    } else {
+        if (later >= L) wait_vmcnt<L * IPW>();
+        else wait_slice<IPW, L - 1>(later);
+    }
+}
+
+// Workgroup barrier that orders LDS traffic: the LDS-DMA copies a wave waited for (vmcnt)
+// and the fragment reads it finished before the barrier, against reads and copies after.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// cache policy of buffer loads and stores: sc1 = device scope (coherent across the XCDs'
+// separate L2 caches)
+constexpr int kDeviceScope = 16;
 
 // Buffer resource over `bytes` bytes at p (raw buffer, 32-bit offsets). Loads at offsets
 // >= bytes return zero instead of touching memory.
@@ -130,19 +186,18 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *p, int64_t bytes) {
 // Per-lane LDS-DMA offsets of one workgroup, fixed for the whole K loop. Tile instruction
 // t of wave w (of NW) copies tile rows 8 (NW t + w) .. +7; lane L fills LDS row (L / 8),
 // physical chunk (L % 8), i.e. it loads the logical chunk that swz_chunk maps there (the
-// map is an involution). The activation-scale instruction of wave w copies rows
-// 64 (w % SA_INSTR) .. +63, the weight-scale instruction the scales of the tile's N-blocks
-// (lane = N-block); waves beyond those repeat identical copies, so every wave issues the
-// same INSTR_PER_WAVE vector-memory instructions per slice. Rows past M or N (and N-blocks
-// past the last) lie outside their buffer resource: they read as zero and only feed outputs
-// that are never stored.
+// map is an involution). Activation-scale instruction t copies rows 64 b .. +63 with
+// b = (NW t + w) mod (BM / 64), the weight-scale instruction the scales of the tile's
+// N-blocks (lane = N-block); repeats are identical copies, so every wave issues the same IPW
+// vector-memory instructions per slice.
 // VARIANT makes the type unique to each kernel instantiation: when kernels of different
 // variants shared one DmaPlan type, the host compiler emitted a launch stub for only one of them.
 template <int BM, int BN, int NSTAGE, int NW, int VARIANT>
 struct DmaPlan {
     using S = GemmSmem<BM, BN, NSTAGE, NW>;
     rsrc_t ra, rw, rsa, rsw;
-    uint32_t a_off[S::A_INSTR], w_off[S::W_INSTR], sa_off, sw_off;
+    uint32_t off[S::IPW];
+    int w;
 
     __device__ __forceinline__ DmaPlan(int wave, int lane, const uint8_t *aq, const uint8_t *wq, const float *sa,
                                        const float *sw, int64_t m0, int64_t n0, int64_t M, int64_t N, int64_t K,
@@ -154,47 +209,60 @@ struct DmaPlan {
         rsa = make_rsrc(sa + m0 * nkb, rows_a * nkb * 4);
         const int64_t nb0 = n0 / G_SLICE, nnb = (N + G_SLICE - 1) / G_SLICE;
         rsw = make_rsrc(sw + nb0 * nkb, (nnb - nb0) * nkb * 4);
+        w = wave;
         const int sub = lane >> 3;
 #pragma unroll
         for (int t = 0; t < S::A_INSTR; ++t) {
-            const int row = 8 * (NW * t + wave) + sub;
-            a_off[t] = (uint32_t)(row * K) + (swz_chunk(row, lane & 7) << 4);
+            const int row = 8 * (NW * t + w) + sub;
+            off[t] = (uint32_t)(row * K) + (swz_chunk(row, lane & 7) << 4);
         }
 #pragma unroll
         for (int t = 0; t < S::W_INSTR; ++t) {
-            const int row = 8 * (NW * t + wave) + sub;
-            w_off[t] = (uint32_t)(row * K) + (swz_chunk(row, lane & 7) << 4);
+            const int row = 8 * (NW * t + w) + sub;
+            off[S::A_INSTR + t] = (uint32_t)(row * K) + (swz_chunk(row, lane & 7) << 4);
         }
-        sa_off = (uint32_t)((64 * (wave % S::SA_INSTR) + lane) * nkb * 4);
-        sw_off = (uint32_t)(lane * nkb * 4);
+#pragma unroll
+        for (int t = 0; t < S::SA_INSTR; ++t)
+            off[S::A_INSTR + S::W_INSTR + t] = (uint32_t)((64 * ((NW * t + w) % S::SA_BLOCKS) + lane) * nkb * 4);
+        off[S::IPW - 1] = (uint32_t)(lane * nkb * 4);
     }
 
     // copies of slice kb into stage buffer `base`
-    __device__ __forceinline__ void issue(uint8_t *base, int64_t kb, int wave) const {
+    __device__ __forceinline__ void issue(uint8_t *base, int64_t kb) const {
         const int koff = (int)(kb * G_SLICE), soff = (int)(kb * 4);
 #pragma unroll
         for (int t = 0; t < S::A_INSTR; ++t)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(base + 8 * (NW * t + wave) * G_SLICE), 16,
-                                                     a_off[t], koff, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(base + 8 * (NW * t + w) * G_SLICE), 16, off[t],
+                                                     koff, 0, 0);
 #pragma unroll
         for (int t = 0; t < S::W_INSTR; ++t)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void *)(base + S::A_BYTES + 8 * (NW * t + wave) * G_SLICE),
-                                                     16, w_off[t], koff, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rsa, (lds_void *)(base + S::A_BYTES + S::W_BYTES + (wave % S::SA_INSTR) * 256), 4, sa_off, soff, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void *)(base + S::A_BYTES + 8 * (NW * t + w) * G_SLICE),
+                                                     16, off[S::A_INSTR + t], koff, 0, 0);
+#pragma unroll
+        for (int t = 0; t < S::SA_INSTR; ++t)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rsa, (lds_void *)(base + S::A_BYTES + S::W_BYTES + ((NW * t + w) % S::SA_BLOCKS) * 256), 4,
+                off[S::A_INSTR + S::W_INSTR + t], soff, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsw, (lds_void *)(base + S::A_BYTES + S::W_BYTES + S::SA_BYTES), 4,
-                                                 sw_off, soff, 0, 0);
+                                                 off[S::IPW - 1], soff, 0, 0);
     }
 };
 
-template <int BM, int BN, int NW, int WAVES_M, int NSTAGE, int UNROLL, int OUT_BF16, int EXACT>
-__global__ __launch_bounds__(NW * 64) void block_gemm_kernel(const uint8_t *__restrict__ aq,
-                                                               const float *__restrict__ sa,
-                                                               const uint8_t *__restrict__ wq,
-                                                               const float *__restrict__ sw,
-                                                               void *__restrict__ y, int64_t M,
-                                                               int64_t N, int64_t K, int tiles_m,
-                                                               int tiles_n, int group) {
+// Kernel arguments (one struct so that every tile variant has the same signature).
+struct GemmArgs {
+    const uint8_t *aq;
+    const float *sa;
+    const uint8_t *wq;
+    const float *sw;
+    void *y;
+    float *part;        // split-K partial tiles [splits][tiles][BM * BN], or null
+    uint32_t *count;    // split-K arrival counter per tile, zero between calls
+    int64_t M, N, K;
+    int tiles_m, tiles_n, group, splits;
+};
+
+template <int BM, int BN, int NW, int WAVES_M, int NSTAGE, int OUT_BF16, int EXACT>
+__global__ __launch_bounds__(NW * 64) void block_gemm_kernel(GemmArgs g) {
     using S = GemmSmem<BM, BN, NSTAGE, NW>;
     constexpr int WAVES_N = NW / WAVES_M;
     static_assert(WAVES_M * WAVES_N == NW, "wave grid");
@@ -209,35 +277,35 @@ __global__ __launch_bounds__(NW * 64) void block_gemm_kernel(const uint8_t *__re
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave % WAVES_M, wn = wave / WAVES_M;
 
-    // Tile order. Consecutive workgroups are dealt round-robin over the 8 XCDs, so
+    // Work order. Consecutive workgroups are dealt round-robin over the 8 XCDs, so
     // workgroup b (XCD b % 8, slot b / 8) is first mapped to a logical index such that each
     // XCD walks a contiguous run of logical indices: XCD x owns q + (x < rem) of them starting
-    // at x*q + min(x, rem), q = tiles / 8, rem = tiles % 8 (a bijection). Logical indices
-    // then run down `group` tile rows before moving one tile column right, so the tiles an
-    // XCD holds at once form a compact block and share A and W panels in its L2.
-    const int tiles = tiles_m * tiles_n;
+    // at x*q + min(x, rem), q = units / 8, rem = units % 8 (a bijection). The split index is
+    // the slowest-varying part of the logical index; within one split, logical tiles run down
+    // `group` tile rows before moving one tile column right, so the tiles an XCD holds at
+    // once form a compact block and share A and W panels in its L2.
+    const int tiles = g.tiles_m * g.tiles_n;
+    const int units = tiles * g.splits;
     const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-    const int q = tiles >> 3, rem = tiles & 7;
+    const int q = units >> 3, rem = units & 7;
     const int logical = xcd * q + (xcd < rem ? xcd : rem) + slot;
-    const int band = logical / (group * tiles_n);                 // band of `group` tile rows
-    const int in_band = logical - band * group * tiles_n;
-    const int band_rows = min(group, tiles_m - band * group);
-    const int tile_m = band * group + in_band % band_rows;
+    const int split = logical / tiles;
+    const int tl = logical - split * tiles;
+    const int band = tl / (g.group * g.tiles_n);                 // band of `group` tile rows
+    const int in_band = tl - band * g.group * g.tiles_n;
+    const int band_rows = min(g.group, g.tiles_m - band * g.group);
+    const int tile_m = band * g.group + in_band % band_rows;
     const int tile_n = in_band / band_rows;
+    const int64_t M = g.M, N = g.N, K = g.K;
     const int64_t m0 = (int64_t)tile_m * BM, n0 = (int64_t)tile_n * BN;
     const int64_t nkb = K / G_SLICE;
+    const int64_t kb0 = split * nkb / g.splits, kb1 = (split + 1) * nkb / g.splits;
 
     f32x4 acc[SUB_M][SUB_N];
 #pragma unroll
     for (int i = 0; i < SUB_M; ++i)
 #pragma unroll
         for (int j = 0; j < SUB_N; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    const DmaPlan<BM, BN, NSTAGE, NW, UNROLL * 4 + OUT_BF16 * 2 + EXACT> dma(wave, lane, aq, wq, sa, sw, m0, n0, M, N, K, nkb);
-    // prologue: slices 0 .. NSTAGE-2 in flight
-#pragma unroll
-    for (int st = 0; st < NSTAGE - 1; ++st)
-        if (st < nkb) dma.issue(smem + st * S::STAGE, st, wave);
 
     const int frow = lane & 15, kgroup = lane >> 4;
     // index of each n-subtile's N-block among the tile's N-blocks
@@ -246,81 +314,71 @@ __global__ __launch_bounds__(NW * 64) void block_gemm_kernel(const uint8_t *__re
 #pragma unroll
     for (int j = 0; j < SUB_N; ++j) sw_idx[j] = (int)(((n0 % G_SLICE) + wn * WN + 16 * j) / G_SLICE);
 
-    // K loop; with UNROLL the stage index (and so every stage buffer offset) is a constant
-    constexpr int U = UNROLL ? NSTAGE : 1;
-    for (int64_t kb0 = 0; kb0 < nkb; kb0 += U) {
+    if (kb0 < kb1) {
+        const DmaPlan<BM, BN, NSTAGE, NW, OUT_BF16 * 2 + EXACT> dma(wave, lane, g.aq, g.wq, g.sa, g.sw, m0, n0, M, N,
+                                                                   K, nkb);
+        // prologue: the first NSTAGE slices in flight
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t kb = kb0 + u;
-            if (kb >= nkb) break;
-            const int st = UNROLL ? u : (int)(kb % NSTAGE);
-            // slice kb has landed once at most (NSTAGE - 2) later slices are outstanding
-            if (kb + NSTAGE - 2 < nkb) wait_vmcnt<(NSTAGE - 2) * S::INSTR_PER_WAVE>();
-            else wait_vmcnt<0>();
-            __builtin_amdgcn_s_barrier();
-            // every wave has finished slice kb-1, whose buffer now receives slice kb + NSTAGE - 1
-            if (kb + NSTAGE - 1 < nkb) dma.issue(smem + ((st + NSTAGE - 1) % NSTAGE) * S::STAGE, kb + NSTAGE - 1, wave);
+        for (int st = 0; st < NSTAGE; ++st)
+            if (kb0 + st < kb1) dma.issue(smem + st * S::STAGE, kb0 + st);
+        wait_slice<S::IPW, NSTAGE - 1>((int)min64(NSTAGE, kb1 - kb0) - 1);
+        lds_barrier();
 
-            const uint8_t *stage = smem + st * S::STAGE;
-            const uint8_t *tA = stage, *tW = stage + S::A_BYTES;
+        // fragments of the slice being contracted
+        i32x8 wf[SUB_N];
+        Frag16 wh[EXACT ? SUB_N : 1];
+        float swv[SUB_N];
+        i32x8 af;
+        float sav;
+        auto load_slice_head = [&](const uint8_t *stage) {
+            const uint8_t *tW = stage + S::A_BYTES;
             const float *tS = reinterpret_cast<const float *>(stage + S::A_BYTES + S::W_BYTES);
             const float *tSW = reinterpret_cast<const float *>(stage + S::A_BYTES + S::W_BYTES + S::SA_BYTES);
-            float swv[SUB_N];
-#pragma unroll
-            for (int j = 0; j < SUB_N; ++j) swv[j] = ONE_SW ? tSW[sw_idx[0]] : tSW[sw_idx[j]];
-
-            i32x8 wf[SUB_N];
 #pragma unroll
             for (int j = 0; j < SUB_N; ++j) wf[j] = load_frag(tW, wn * WN + 16 * j + frow, kgroup);
-            Frag16 wh[EXACT ? SUB_N : 1];
+            af = load_frag(stage, wm * WM + frow, kgroup);
+            sav = tS[wm * WM + frow];
+#pragma unroll
+            for (int j = 0; j < SUB_N; ++j) swv[j] = ONE_SW ? tSW[sw_idx[0]] : tSW[sw_idx[j]];
             if constexpr (EXACT) {
 #pragma unroll
                 for (int j = 0; j < SUB_N; ++j) wh[j] = to_f16(wf[j]);
             }
-            // A fragments are read one 16-row group ahead of the MFMAs that consume them, and
-            // the promotion of group i-1 is interleaved with the MFMAs of group i
-            i32x8 af = load_frag(tA, wm * WM + frow, kgroup);
-            float sav = tS[wm * WM + frow];
-            f32x4 p_prev[SUB_N];
-            float f_prev[SUB_N];
+        };
+        load_slice_head(smem);
+
+        f32x4 p_prev[SUB_N];
+        float f_prev[SUB_N];
+        int st = 0;
+        for (int64_t kb = kb0; kb < kb1; ++kb) {
+            const uint8_t *stage = smem + st * S::STAGE;
+            const float *tS = reinterpret_cast<const float *>(stage + S::A_BYTES + S::W_BYTES);
 #pragma unroll
             for (int i = 0; i < SUB_M; ++i) {
-                i32x8 af_next = af;
-                float sav_next = sav;
+                i32x8 af_n = af;
+                float sav_n = sav;
                 if (i + 1 < SUB_M) {
-                    af_next = load_frag(tA, wm * WM + 16 * (i + 1) + frow, kgroup);
-                    sav_next = tS[wm * WM + 16 * (i + 1) + frow];
+                    af_n = load_frag(stage, wm * WM + 16 * (i + 1) + frow, kgroup);
+                    sav_n = tS[wm * WM + 16 * (i + 1) + frow];
                 }
-                f32x4 p_cur[SUB_N];
                 float f_cur[SUB_N];
-                if constexpr (ONE_SW) {
-                    const float f = sav * swv[0];
 #pragma unroll
-                    for (int j = 0; j < SUB_N; ++j) f_cur[j] = f;
-                } else {
-#pragma unroll
-                    for (int j = 0; j < SUB_N; ++j) f_cur[j] = sav * swv[j];
-                }
+                for (int j = 0; j < SUB_N; ++j) f_cur[j] = sav * (ONE_SW ? swv[0] : swv[j]);
+                f32x4 p_cur[SUB_N];
                 if constexpr (EXACT) {
                     const Frag16 ah = to_f16(af);
 #pragma unroll
                     for (int j = 0; j < SUB_N; ++j) {
                         p_cur[j] = mfma_slice_exact(wh[j], ah);
-                        if (i > 0) {
-#pragma unroll
-                            for (int r = 0; r < 4; ++r)
-                                acc[i - 1][j][r] = __builtin_fmaf(p_prev[j][r], f_prev[j], acc[i - 1][j][r]);
-                        }
+                        if (i > 0) promote(acc[i - 1][j], p_prev[j], f_prev[j]);
+                        __builtin_amdgcn_sched_barrier(0);
                     }
                 } else {
 #pragma unroll
                     for (int j = 0; j < SUB_N; ++j) {
                         p_cur[j] = mfma_slice(wf[j], af);
-                        if (i > 0) {
-#pragma unroll
-                            for (int r = 0; r < 4; ++r)
-                                acc[i - 1][j][r] = __builtin_fmaf(p_prev[j][r], f_prev[j], acc[i - 1][j][r]);
-                        }
+                        if (i > 0) promote(acc[i - 1][j], p_prev[j], f_prev[j]);
+                        __builtin_amdgcn_sched_barrier(0);
                     }
                 }
 #pragma unroll
@@ -328,15 +386,68 @@ __global__ __launch_bounds__(NW * 64) void block_gemm_kernel(const uint8_t *__re
                     p_prev[j] = p_cur[j];
                     f_prev[j] = f_cur[j];
                 }
-                af = af_next;
-                sav = sav_next;
+                af = af_n;
+                sav = sav_n;
+            }
+            // the last group's MFMAs are in flight: move on to the next slice meanwhile
+            const int st_next = st + 1 == NSTAGE ? 0 : st + 1;
+            if (kb + 1 < kb1) {
+                wait_slice<S::IPW, NSTAGE - 2>((int)min64(NSTAGE - 2, kb1 - 1 - (kb + 1)));
+                lds_barrier();
+                // every wave is done with slice kb: its buffer receives slice kb + NSTAGE
+                if (kb + NSTAGE < kb1) dma.issue(smem + st * S::STAGE, kb + NSTAGE);
+                load_slice_head(smem + st_next * S::STAGE);
             }
 #pragma unroll
-            for (int j = 0; j < SUB_N; ++j)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    acc[SUB_M - 1][j][r] = __builtin_fmaf(p_prev[j][r], f_prev[j], acc[SUB_M - 1][j][r]);
+            for (int j = 0; j < SUB_N; ++j) promote(acc[SUB_M - 1][j], p_prev[j], f_prev[j]);
+            __builtin_amdgcn_sched_barrier(0);
+            st = st_next;
         }
+    }
+
+    if (g.splits > 1) {
+        // split-K: publish this split's partial tile (fragment order: one 1 KiB line per
+        // (wave, i, j), lane-contiguous) with device-coherent stores (sc1: written through
+        // to memory, visible to every XCD once the store has completed), then count
+        // arrivals. No release/acquire fence is used: at device scope those write back or
+        // invalidate the whole L2, which costs more than the partials themselves; the
+        // partial traffic itself is coherent and the counter is bumped only after the
+        // stores have completed (vmcnt 0).
+        const rsrc_t rp = make_rsrc(g.part + (int64_t)tl * g.splits * (BM * BN), (int64_t)g.splits * BM * BN * 4);
+        const uint32_t lane_off = (uint32_t)((wave * (SUB_M * SUB_N * 64) + lane) * 16);
+        const int split_off = split * (BM * BN * 4);
+#pragma unroll
+        for (int i = 0; i < SUB_M; ++i)
+#pragma unroll
+            for (int j = 0; j < SUB_N; ++j)
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, acc[i][j]), rp,
+                                                       lane_off + (i * SUB_N + j) * 1024, split_off, kDeviceScope);
+        wait_vmcnt<0>();
+        __syncthreads();
+        int *flag = reinterpret_cast<int *>(smem + S::FLAG);
+        if (threadIdx.x == 0) {
+            const uint32_t old = __hip_atomic_fetch_add(&g.count[tl], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const int last = old == (uint32_t)(g.splits - 1);
+            if (last) __hip_atomic_store(&g.count[tl], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            *flag = last;
+        }
+        __syncthreads();
+        if (!*flag) return;
+        // the last to arrive sums the partials in split order (independent of which split
+        // arrived last), one 16x16 block at a time, with device-coherent loads
+#pragma unroll
+        for (int i = 0; i < SUB_M; ++i)
+#pragma unroll
+            for (int j = 0; j < SUB_N; ++j) {
+                const uint32_t o = lane_off + (i * SUB_N + j) * 1024;
+                f32x4 t = split == 0 ? acc[i][j]
+                                     : __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rp, o, 0, kDeviceScope));
+                for (int sp = 1; sp < g.splits; ++sp)
+                    t += sp == split ? acc[i][j]
+                                     : __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                                     rp, o, sp * (BM * BN * 4), kDeviceScope));
+                acc[i][j] = t;
+            }
     }
 
     // epilogue: lane holds Y[m][n .. n+3] for each (i, j)
@@ -351,7 +462,7 @@ __global__ __launch_bounds__(NW * 64) void block_gemm_kernel(const uint8_t *__re
             if (n >= N) continue;
             const f32x4 v = acc[i][j];
             if constexpr (OUT_BF16) {
-                uint16_t *yp = reinterpret_cast<uint16_t *>(y) + m * N + n;
+                uint16_t *yp = reinterpret_cast<uint16_t *>(g.y) + m * N + n;
                 const uint32_t lo = pack_bf16x2(v[0], v[1]), hi = pack_bf16x2(v[2], v[3]);
                 if (vec_ok && n + 3 < N) {
                     *reinterpret_cast<u32x2 *>(yp) = u32x2{lo, hi};
@@ -360,7 +471,7 @@ __global__ __launch_bounds__(NW * 64) void block_gemm_kernel(const uint8_t *__re
                     for (int r = 0; r < 4 && n + r < N; ++r) yp[r] = h[r];
                 }
             } else {
-                float *yp = reinterpret_cast<float *>(y) + m * N + n;
+                float *yp = reinterpret_cast<float *>(g.y) + m * N + n;
                 if (vec_ok && n + 3 < N) {
                     *reinterpret_cast<f32x4 *>(yp) = v;
                 } else {
@@ -371,12 +482,38 @@ __global__ __launch_bounds__(NW * 64) void block_gemm_kernel(const uint8_t *__re
     }
 }
 
-size_t gemm_workspace_bytes(int64_t, int64_t, int64_t, bool) { return 0; }
+// ---------------------------------------------------------------------------------------
+// host side: tile and split choice, workspace, launch
+
+// Tile configurations: (BM, BN, waves, waves along M, stages). The timing columns are
+// measured on MI355X (FP8 products, full-size workloads, every CU busy): the duration of
+// one K slice of one tile, and the fixed cost of a tile (first copies in flight, output
+// stores).
+enum GemmTile {
+    T256x256W8 = 0, T256x192W8, T256x128W8, T128x256W8, T128x192, T256x128, T128x128, T_COUNT
+};
+
+struct TileInfo {
+    const char *name;
+    int bm, bn;
+    bool fp8_ok, exact_ok;
+    double us_slice, us_fixed;
+};
+
+static const TileInfo kTiles[T_COUNT] = {
+    {"256x256w8", 256, 256, true, false, 2.46, 14.5}, {"256x192w8", 256, 192, true, false, 2.04, 10.0},
+    {"256x128w8", 256, 128, true, false, 1.62, 5.8},  {"128x256w8", 128, 256, true, false, 1.58, 6.0},
+    {"128x192", 128, 192, true, false, 1.19, 4.4},    {"256x128", 256, 128, true, false, 1.44, 5.8},
+    {"128x128", 128, 128, true, true, 1.05, 3.0},
+};
+
+constexpr int kNumCUs = 256;
+constexpr int kMaxSplits = 8;
 
 // Rows of A plus rows of W that the first concurrent tiles of one XCD touch when logical
 // tiles run down `group` tile rows at a time (each XCD holds about cus_per_xcd tiles).
 static int64_t xcd_panel_rows(int64_t tiles_m, int64_t tiles_n, int64_t group, int64_t bm, int64_t bn) {
-    const int64_t cus_per_xcd = 32;
+    const int64_t cus_per_xcd = kNumCUs / 8;
     const int64_t g = group < tiles_m ? group : tiles_m;
     const int64_t cols = (cus_per_xcd + g - 1) / g;
     return g * bm + (cols < tiles_n ? cols : tiles_n) * bn;
@@ -395,67 +532,118 @@ static int choose_group(int64_t tiles_m, int64_t tiles_n, int64_t bm, int64_t bn
     return best;
 }
 
-template <int BM, int BN, int NW, int WAVES_M, int NSTAGE, int UNROLL, int EXACT>
-static hipError_t launch_cfg(const uint8_t *aq, const float *sa, const uint8_t *wq, const float *sw, void *y,
-                             bool out_bf16, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
-    const int64_t tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-    const int group = choose_group(tiles_m, tiles_n, BM, BN);
-    const dim3 grid((unsigned)(tiles_m * tiles_n)), block(NW * 64);
-    if (out_bf16)
-        block_gemm_kernel<BM, BN, NW, WAVES_M, NSTAGE, UNROLL, 1, EXACT><<<grid, block, 0, stream>>>(
-            aq, sa, wq, sw, y, M, N, K, (int)tiles_m, (int)tiles_n, group);
-    else
-        block_gemm_kernel<BM, BN, NW, WAVES_M, NSTAGE, UNROLL, 0, EXACT><<<grid, block, 0, stream>>>(
-            aq, sa, wq, sw, y, M, N, K, (int)tiles_m, (int)tiles_n, group);
-    return hipGetLastError();
-}
-
-// Tile configurations of the FP8-matrix-unit path: (BM, BN, waves, waves along M, stages).
-enum GemmTile {
-    T256x128 = 0, T256x128U, T128x128, T256x128W8, T256x128W8U, T256x256W8,
-    T128x192, T128x192U, T128x256W8, T128x256W8U, T_COUNT
+struct GemmPlan {
+    int tile, splits;
+    int64_t tiles_m, tiles_n;
 };
 
-static const char *const kTileNames[T_COUNT] = {"256x128",   "256x128u",  "128x128", "256x128w8",
-                                                "256x128w8u", "256x256w8", "128x192", "128x192u",
-                                                "128x256w8", "128x256w8u"};
-
-// Shape -> tile. FP8Q_GEMM_TILE (one of kTileNames) overrides the choice; it exists for
-// tuning and is read once.
-static int choose_tile(int64_t M, int64_t N) {
-    static const int forced = [] {
+// Tuning overrides, read once: FP8Q_GEMM_TILE (a tile name) and FP8Q_GEMM_SPLITS.
+static int env_tile() {
+    static const int v = [] {
         const char *e = std::getenv("FP8Q_GEMM_TILE");
         if (e)
             for (int t = 0; t < T_COUNT; ++t)
-                if (std::strcmp(e, kTileNames[t]) == 0) return t;
+                if (std::strcmp(e, kTiles[t].name) == 0) return t;
         return -1;
     }();
-    if (forced >= 0) return forced;
-    (void)M;
-    (void)N;
-    return T256x128;
+    return v;
+}
+static int env_splits() {
+    static const int v = [] {
+        const char *e = std::getenv("FP8Q_GEMM_SPLITS");
+        const int s = e ? std::atoi(e) : 0;
+        return s >= 1 && s <= kMaxSplits ? s : 0;
+    }();
+    return v;
+}
+
+// Split-K workspace: the arrival counters first, at a fixed place whatever the shape (a
+// later call with another shape must find zeros there), then the partial tiles.
+constexpr int64_t kMaxSplitTiles = 4096;
+constexpr size_t kCounterBytes = kMaxSplitTiles * sizeof(uint32_t);
+
+static size_t split_bytes(const GemmPlan &p) {
+    if (p.splits <= 1) return 0;
+    const int64_t tiles = p.tiles_m * p.tiles_n;
+    return kCounterBytes + (size_t)tiles * p.splits * kTiles[p.tile].bm * kTiles[p.tile].bn * sizeof(float);
+}
+
+// Estimated duration (us): full waves of workgroups times the slices each contracts plus
+// its fixed cost, plus the split-K reduction (the last workgroup of a tile reads the other
+// splits' partials; all of them write theirs).
+static double plan_cost(int tile, int64_t tiles, int splits, int64_t nkb) {
+    const TileInfo &t = kTiles[tile];
+    const double kouts = t.bm * t.bn / 1024.0;
+    const int64_t units = tiles * splits;
+    const int64_t waves = (units + kNumCUs - 1) / kNumCUs;
+    const double per_unit = (double)((nkb + splits - 1) / splits) * t.us_slice + t.us_fixed;
+    return waves * per_unit + (splits - 1) * 0.23 * kouts;
+}
+
+static GemmPlan make_plan(int64_t M, int64_t N, int64_t K, bool exact, size_t ws_bytes, bool size_query) {
+    const int64_t nkb = K / G_SLICE;
+    GemmPlan best{T128x128, 1, (M + 127) / 128, (N + 127) / 128};
+    double best_cost = 1e300;
+    const int forced_tile = exact ? -1 : env_tile(), forced_splits = exact ? 1 : env_splits();
+    for (int t = 0; t < T_COUNT; ++t) {
+        if (exact ? !kTiles[t].exact_ok : !kTiles[t].fp8_ok) continue;
+        if (forced_tile >= 0 && t != forced_tile) continue;
+        const int64_t tm = (M + kTiles[t].bm - 1) / kTiles[t].bm, tn = (N + kTiles[t].bn - 1) / kTiles[t].bn;
+        for (int s = 1; s <= (exact ? 1 : kMaxSplits); ++s) {
+            // a split contracts at least 2 slices; a forced count falls back to 1 where it cannot apply
+            if (s > 1 && (nkb < 2 * s || tm * tn > kMaxSplitTiles)) break;
+            const GemmPlan p{t, s, tm, tn};
+            if (s > 1 && !size_query && split_bytes(p) > ws_bytes) break;
+            if (forced_splits && s != forced_splits && s != 1) continue;
+            double c = plan_cost(t, tm * tn, s, nkb);
+            if (forced_splits && s == 1 && forced_splits != 1) c += 1e200;   // only if the forced count is impossible
+            if (c < best_cost) {
+                best_cost = c;
+                best = p;
+            }
+        }
+    }
+    return best;
+}
+
+size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, bool, bool exact) {
+    return split_bytes(make_plan(M, N, K, exact, 0, true));
+}
+
+template <int BM, int BN, int NW, int WAVES_M, int NSTAGE, int EXACT>
+static hipError_t launch_cfg(GemmArgs a, bool out_bf16, int splits, hipStream_t stream) {
+    a.tiles_m = (int)((a.M + BM - 1) / BM);
+    a.tiles_n = (int)((a.N + BN - 1) / BN);
+    a.group = choose_group(a.tiles_m, a.tiles_n, BM, BN);
+    a.splits = splits;
+    const dim3 grid((unsigned)((int64_t)a.tiles_m * a.tiles_n * splits)), block(NW * 64);
+    if (out_bf16)
+        block_gemm_kernel<BM, BN, NW, WAVES_M, NSTAGE, 1, EXACT><<<grid, block, 0, stream>>>(a);
+    else
+        block_gemm_kernel<BM, BN, NW, WAVES_M, NSTAGE, 0, EXACT><<<grid, block, 0, stream>>>(a);
+    return hipGetLastError();
 }
 
 hipError_t launch_block_gemm(const uint8_t *aq, const float *sa, const uint8_t *wq, const float *sw,
-                             void *y, bool out_bf16, bool exact, int64_t M, int64_t N, int64_t K, void *, size_t,
-                             hipStream_t stream) {
+                             void *y, bool out_bf16, bool exact, int64_t M, int64_t N, int64_t K, void *workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
     if (M == 0 || N == 0) return hipSuccess;
-    if (exact) return launch_cfg<128, 128, 4, 2, 4, 0, 1>(aq, sa, wq, sw, y, out_bf16, M, N, K, stream);
-#define FP8Q_CFG(BM_, BN_, NW_, WM_, NS_, U_) \
-    return launch_cfg<BM_, BN_, NW_, WM_, NS_, U_, 0>(aq, sa, wq, sw, y, out_bf16, M, N, K, stream)
-    switch (choose_tile(M, N)) {
-    case T256x128U: FP8Q_CFG(256, 128, 4, 2, 3, 1);
-    case T128x128: FP8Q_CFG(128, 128, 4, 2, 4, 0);
-    case T256x128W8: FP8Q_CFG(256, 128, 8, 4, 3, 0);
-    case T256x128W8U: FP8Q_CFG(256, 128, 8, 4, 3, 1);
-    case T256x256W8: FP8Q_CFG(256, 256, 8, 2, 2, 0);
-    case T128x192: FP8Q_CFG(128, 192, 4, 2, 3, 0);
-    case T128x192U: FP8Q_CFG(128, 192, 4, 2, 3, 1);
-    case T128x256W8: FP8Q_CFG(128, 256, 8, 2, 3, 0);
-    case T128x256W8U: FP8Q_CFG(128, 256, 8, 2, 3, 1);
-    default: FP8Q_CFG(256, 128, 4, 2, 3, 0);
+    const GemmPlan p = make_plan(M, N, K, exact, workspace ? workspace_bytes : 0, false);
+    GemmArgs a{aq, sa, wq, sw, y, nullptr, nullptr, M, N, K, 0, 0, 1, 1};
+    if (p.splits > 1) {
+        a.count = static_cast<uint32_t *>(workspace);
+        a.part = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + kCounterBytes);
     }
-#undef FP8Q_CFG
+    if (exact) return launch_cfg<128, 128, 4, 2, 4, 1>(a, out_bf16, 1, stream);
+    switch (p.tile) {
+    case T256x256W8: return launch_cfg<256, 256, 8, 2, 2, 0>(a, out_bf16, p.splits, stream);
+    case T256x192W8: return launch_cfg<256, 192, 8, 2, 2, 0>(a, out_bf16, p.splits, stream);
+    case T256x128W8: return launch_cfg<256, 128, 8, 4, 3, 0>(a, out_bf16, p.splits, stream);
+    case T128x256W8: return launch_cfg<128, 256, 8, 2, 3, 0>(a, out_bf16, p.splits, stream);
+    case T128x192: return launch_cfg<128, 192, 4, 2, 3, 0>(a, out_bf16, p.splits, stream);
+    case T256x128: return launch_cfg<256, 128, 4, 2, 3, 0>(a, out_bf16, p.splits, stream);
+    default: return launch_cfg<128, 128, 4, 2, 4, 0>(a, out_bf16, p.splits, stream);
+    }
 }
 
 }  // namespace fp8q

@@ -118,17 +118,23 @@ int fp8_weight_dequant(const uint8_t *q, const float *s, uint16_t *w, int64_t N,
  *      the fp32 accumulator). With K = 0 the output is all zeros.
  *   aq, wq, y: 16-byte aligned; sa, sw: 4-byte aligned. M, N >= 0 arbitrary (ragged tails
  *   are masked), K a multiple of 128 and at most 2^24.
- *   workspace / workspace_bytes: optional device scratch for a split-K schedule; pass
- *   NULL / 0 to run without it. If workspace_bytes is smaller than
- *   fp8_block_gemm_workspace_bytes() the call runs without split-K (it does not fail).
+ *   workspace / workspace_bytes: optional device scratch (16-byte aligned) for a split-K
+ *   schedule, used by shapes with too few output tiles to fill the GPU; pass NULL / 0 to run
+ *   without it. If workspace_bytes is smaller than fp8_block_gemm_workspace_bytes() the call
+ *   runs without split-K (it does not fail). The workspace must be zero-filled before its
+ *   first use; every call that completes leaves it ready for the next (its arrival counters
+ *   back at zero), so zero it once and reuse it. Calls that may run at the same time must
+ *   not share a workspace.
  *   The result does not depend on whether a workspace is given beyond fp32 rounding
- *   order, and is deterministic for a given (M, N, K, workspace) call. */
+ *   order (split-K sums the K ranges' fp32 partials in a fixed order), and is deterministic
+ *   for a given (M, N, K, workspace size) call. */
 int fp8_block_gemm(const uint8_t *aq, const float *sa, const uint8_t *wq, const float *sw,
                    void *y, int y_dtype, int64_t M, int64_t N, int64_t K, void *workspace,
                    size_t workspace_bytes, void *stream);
 
 /* Workspace size in bytes that lets fp8_block_gemm use its split-K schedule for this
- * shape (0 if the shape does not use one). Host-only; enqueues nothing. */
+ * shape and y_dtype (including the mode bits); 0 if that call does not use one or the
+ * arguments are invalid. Host-only; enqueues nothing. */
 size_t fp8_block_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int y_dtype);
 
 /* Static string describing a status code (never NULL). */

@@ -187,6 +187,43 @@ def test_gemm_deterministic(mode):
     assert torch.equal(y1.view(torch.int32), y2.view(torch.int32))
 
 
+@pytest.mark.parametrize("M,N,K", [(300, 576, 2048), (513, 777, 3072), (1, 1, 1024), (129, 129, 1280)])
+def test_gemm_split_k_workspace(M, N, K):
+    """Shapes with few output tiles split K over several workgroups when a workspace is
+    given. The split result meets the bound like the unsplit one, repeats bit for bit
+    with a reused workspace (the arrival counters are reset by every call, also after the
+    workspace served another shape), and differs from the unsplit result only by fp32
+    rounding order."""
+    need = fq.gemm_workspace_bytes(M, N, K, torch.bfloat16)
+    assert need > 0, "shape expected to use split-K"
+    A = synth.random_bf16((M, K), seed=7 * M + K)
+    W = synth.random_bf16((N, K), seed=11 * N + K, std=0.02)
+    print(f"split-K {M}x{N}x{K} workspace {need} B", flush=True)
+    aq, sa, wq, sw = quantise_on_gpu(A, W)
+    ws = torch.zeros(need + (1 << 20), dtype=torch.uint8, device="cuda")
+    y1 = fq.fp8_gemm(aq, sa, wq, sw, out_dtype=torch.float32, mode="fp8", workspace=ws)
+    # the same workspace for another shape in between
+    B = synth.random_bf16((700, K), seed=3)
+    bq, sb = fq.act_quant(dev_bf16(B))
+    fq.fp8_gemm(bq, sb, wq, sw, out_dtype=torch.bfloat16, mode="fp8", workspace=ws)
+    y2 = fq.fp8_gemm(aq, sa, wq, sw, out_dtype=torch.float32, mode="fp8", workspace=ws)
+    y0 = fq.fp8_gemm(aq, sa, wq, sw, out_dtype=torch.float32, mode="fp8", workspace=None)
+    yb = fq.fp8_gemm(aq, sa, wq, sw, out_dtype=torch.bfloat16, mode="fp8", workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int32), y2.view(torch.int32))
+    haq, hsa, hwq, hsw = host_codes(aq), sa.cpu().numpy(), host_codes(wq), sw.cpu().numpy()
+    y_hat, bound = oracle.block_gemm(haq, hsa, hwq, hsw)
+    rows, cols = np.repeat(np.arange(M), N), np.tile(np.arange(N), M)
+    allowance = (scale_floor(haq, hwq, rows, cols) +
+                 mfma_group_allowance(haq, hsa, hwq, hsw, rows, cols)).reshape(M, N)
+    for y, out in ((y1, "f32"), (y0, "f32"), (yb, "bf16")):
+        res = gemm_check(y_host(y, out), y_hat, bound, out, allowance)
+        assert res["violations"] == 0, (out, res)
+    # split and unsplit sums differ only in fp32 rounding order: a few ulp of sum |partial * scale|
+    d = np.abs(y1.cpu().numpy().astype(np.float64) - y0.cpu().numpy().astype(np.float64))
+    assert np.all(d <= 2.0 ** -17 * bound + 1e-30), float(np.max(d / np.maximum(bound, 1e-300)))
+
+
 @pytest.mark.parametrize("name", ["q_down", "kv_down", "kv_up", "outlier"])
 def test_gemm_workload_full_size_sampled(name):
     wl = synth.WORKLOADS[name]
