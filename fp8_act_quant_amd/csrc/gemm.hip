@@ -71,7 +71,8 @@ struct GemmSmem {
     static constexpr int SA_BYTES = BM * 4;
     static constexpr int SW_BYTES = 64 * 4;   // weight scales of 64 N-blocks from the tile's first
     static constexpr int STAGE = A_BYTES + W_BYTES + SA_BYTES + SW_BYTES;
-    static constexpr int FLAG = STAGE * NSTAGE;   // split-K "last to arrive" flag
+    static constexpr int DUMMY = STAGE * NSTAGE;   // 256-byte landing area of padding copies
+    static constexpr int FLAG = DUMMY + 256;       // split-K "last to arrive" flag
     static constexpr int TOTAL = FLAG + 16;
     // LDS-DMA instructions per wave and slice: each tile instruction moves 1 KiB (8 rows of
     // 128 B), each scale instruction 256 B (64 rows of one fp32)
@@ -186,10 +187,13 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *p, int64_t bytes) {
 // Per-lane LDS-DMA offsets of one workgroup, fixed for the whole K loop. Tile instruction
 // t of wave w (of NW) copies tile rows 8 (NW t + w) .. +7; lane L fills LDS row (L / 8),
 // physical chunk (L % 8), i.e. it loads the logical chunk that swz_chunk maps there (the
-// map is an involution). Activation-scale instruction t copies rows 64 b .. +63 with
-// b = (NW t + w) mod (BM / 64), the weight-scale instruction the scales of the tile's
-// N-blocks (lane = N-block); repeats are identical copies, so every wave issues the same IPW
-// vector-memory instructions per slice.
+// map is an involution). Activation-scale instruction t of wave w copies rows 64 b .. +63,
+// b = NW t + w; where b >= BM / 64 the instruction only pads the count (every wave issues
+// the same IPW vector-memory instructions per slice) and reads one line into a dummy LDS
+// area. The weight-scale instruction copies the scales of the (at most 3) N-blocks the tile
+// spans, lane = N-block; the other lanes repeat lane 0's address, so they add no line
+// requests. (Each scale instruction addresses one line per active distinct row, so these
+// paddings would otherwise cost as many line requests as the tile rows themselves.)
 // VARIANT makes the type unique to each kernel instantiation: when kernels of different
 // variants shared one DmaPlan type, the host compiler emitted a launch stub for only one of them.
 template <int BM, int BN, int NSTAGE, int NW, int VARIANT>
@@ -198,10 +202,11 @@ struct DmaPlan {
     rsrc_t ra, rw, rsa, rsw;
     uint32_t off[S::IPW];
     int w;
+    uint8_t *dummy;
 
     __device__ __forceinline__ DmaPlan(int wave, int lane, const uint8_t *aq, const uint8_t *wq, const float *sa,
                                        const float *sw, int64_t m0, int64_t n0, int64_t M, int64_t N, int64_t K,
-                                       int64_t nkb) {
+                                       int64_t nkb, uint8_t *smem_dummy) {
         const int64_t rows_a = (M - m0) < BM ? (M - m0) : BM;
         const int64_t rows_w = (N - n0) < BN ? (N - n0) : BN;
         ra = make_rsrc(aq + m0 * K, rows_a * K);
@@ -210,6 +215,7 @@ struct DmaPlan {
         const int64_t nb0 = n0 / G_SLICE, nnb = (N + G_SLICE - 1) / G_SLICE;
         rsw = make_rsrc(sw + nb0 * nkb, (nnb - nb0) * nkb * 4);
         w = wave;
+        dummy = smem_dummy;
         const int sub = lane >> 3;
 #pragma unroll
         for (int t = 0; t < S::A_INSTR; ++t) {
@@ -222,29 +228,49 @@ struct DmaPlan {
             off[S::A_INSTR + t] = (uint32_t)(row * K) + (swz_chunk(row, lane & 7) << 4);
         }
 #pragma unroll
-        for (int t = 0; t < S::SA_INSTR; ++t)
-            off[S::A_INSTR + S::W_INSTR + t] = (uint32_t)((64 * ((NW * t + w) % S::SA_BLOCKS) + lane) * nkb * 4);
-        off[S::IPW - 1] = (uint32_t)(lane * nkb * 4);
+        for (int t = 0; t < S::SA_INSTR; ++t) {
+            const int b = NW * t + w;
+            off[S::A_INSTR + S::W_INSTR + t] = b < S::SA_BLOCKS ? (uint32_t)((64 * b + lane) * nkb * 4) : 0u;
+        }
+        off[S::IPW - 1] = (uint32_t)((lane < 4 ? lane : 0) * nkb * 4);
     }
 
-    // copies of slice kb into stage buffer `base`
+    // instruction I (of IPW) of the copies of slice kb into stage buffer `base`; I is a
+    // constant wherever this is inlined (the loops that call it are unrolled)
+    __device__ __forceinline__ void issue_one(uint8_t *base, int koff, int soff, int I) const {
+        if (I < S::A_INSTR) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(base + 8 * (NW * I + w) * G_SLICE), 16, off[I],
+                                                     koff, 0, 0);
+        } else if (I < S::A_INSTR + S::W_INSTR) {
+            const int t = I - S::A_INSTR;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void *)(base + S::A_BYTES + 8 * (NW * t + w) * G_SLICE),
+                                                     16, off[I], koff, 0, 0);
+        } else if (I < S::IPW - 1) {
+            const int b = NW * (I - S::A_INSTR - S::W_INSTR) + w;
+            uint8_t *dst = b < S::SA_BLOCKS ? base + S::A_BYTES + S::W_BYTES + b * 256 : dummy;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_void *)dst, 4, off[I], soff, 0, 0);
+        } else {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsw, (lds_void *)(base + S::A_BYTES + S::W_BYTES + S::SA_BYTES),
+                                                     4, off[I], soff, 0, 0);
+        }
+    }
+
+    // all copies of slice kb into stage buffer `base`
     __device__ __forceinline__ void issue(uint8_t *base, int64_t kb) const {
         const int koff = (int)(kb * G_SLICE), soff = (int)(kb * 4);
 #pragma unroll
-        for (int t = 0; t < S::A_INSTR; ++t)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(base + 8 * (NW * t + w) * G_SLICE), 16, off[t],
-                                                     koff, 0, 0);
+        for (int I = 0; I < S::IPW; ++I) issue_one(base, koff, soff, I);
+    }
+
+    // part g of NG (g a constant after unrolling) of the copies of slice kb: instructions
+    // [g * PER, min((g + 1) * PER, IPW)), PER = ceil(IPW / NG)
+    template <int NG>
+    __device__ __forceinline__ void issue_part(uint8_t *base, int64_t kb, int g) const {
+        constexpr int PER = (S::IPW + NG - 1) / NG;
+        const int koff = (int)(kb * G_SLICE), soff = (int)(kb * 4);
 #pragma unroll
-        for (int t = 0; t < S::W_INSTR; ++t)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void *)(base + S::A_BYTES + 8 * (NW * t + w) * G_SLICE),
-                                                     16, off[S::A_INSTR + t], koff, 0, 0);
-#pragma unroll
-        for (int t = 0; t < S::SA_INSTR; ++t)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rsa, (lds_void *)(base + S::A_BYTES + S::W_BYTES + ((NW * t + w) % S::SA_BLOCKS) * 256), 4,
-                off[S::A_INSTR + S::W_INSTR + t], soff, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsw, (lds_void *)(base + S::A_BYTES + S::W_BYTES + S::SA_BYTES), 4,
-                                                 off[S::IPW - 1], soff, 0, 0);
+        for (int c = 0; c < PER; ++c)
+            if (g * PER + c < S::IPW) issue_one(base, koff, soff, g * PER + c);
     }
 };
 
@@ -316,7 +342,7 @@ __global__ __launch_bounds__(NW * 64) void block_gemm_kernel(GemmArgs g) {
 
     if (kb0 < kb1) {
         const DmaPlan<BM, BN, NSTAGE, NW, OUT_BF16 * 2 + EXACT> dma(wave, lane, g.aq, g.wq, g.sa, g.sw, m0, n0, M, N,
-                                                                   K, nkb);
+                                                                   K, nkb, smem + S::DUMMY);
         // prologue: the first NSTAGE slices in flight
 #pragma unroll
         for (int st = 0; st < NSTAGE; ++st)
@@ -353,6 +379,11 @@ __global__ __launch_bounds__(NW * 64) void block_gemm_kernel(GemmArgs g) {
         for (int64_t kb = kb0; kb < kb1; ++kb) {
             const uint8_t *stage = smem + st * S::STAGE;
             const float *tS = reinterpret_cast<const float *>(stage + S::A_BYTES + S::W_BYTES);
+            // the copies of slice kb + NSTAGE - 1 go into the buffer of slice kb - 1, free since
+            // the barrier that ended slice kb - 1; they are spread over this slice's row groups
+            // so that the matrix unit is never left waiting behind a burst of copy issues
+            const bool copy_now = kb > kb0 && kb + NSTAGE - 1 < kb1;
+            uint8_t *const copy_dst = smem + (st == 0 ? NSTAGE - 1 : st - 1) * S::STAGE;
 #pragma unroll
             for (int i = 0; i < SUB_M; ++i) {
                 i32x8 af_n = af;
@@ -370,6 +401,7 @@ __global__ __launch_bounds__(NW * 64) void block_gemm_kernel(GemmArgs g) {
 #pragma unroll
                     for (int j = 0; j < SUB_N; ++j) {
                         p_cur[j] = mfma_slice_exact(wh[j], ah);
+                        if (j == 0 && copy_now) dma.template issue_part<SUB_M>(copy_dst, kb + NSTAGE - 1, i);
                         if (i > 0) promote(acc[i - 1][j], p_prev[j], f_prev[j]);
                         __builtin_amdgcn_sched_barrier(0);
                     }
@@ -377,6 +409,7 @@ __global__ __launch_bounds__(NW * 64) void block_gemm_kernel(GemmArgs g) {
 #pragma unroll
                     for (int j = 0; j < SUB_N; ++j) {
                         p_cur[j] = mfma_slice(wf[j], af);
+                        if (j == 0 && copy_now) dma.template issue_part<SUB_M>(copy_dst, kb + NSTAGE - 1, i);
                         if (i > 0) promote(acc[i - 1][j], p_prev[j], f_prev[j]);
                         __builtin_amdgcn_sched_barrier(0);
                     }
@@ -394,8 +427,6 @@ __global__ __launch_bounds__(NW * 64) void block_gemm_kernel(GemmArgs g) {
             if (kb + 1 < kb1) {
                 wait_slice<S::IPW, NSTAGE - 2>((int)min64(NSTAGE - 2, kb1 - 1 - (kb + 1)));
                 lds_barrier();
-                // every wave is done with slice kb: its buffer receives slice kb + NSTAGE
-                if (kb + NSTAGE < kb1) dma.issue(smem + st * S::STAGE, kb + NSTAGE);
                 load_slice_head(smem + st_next * S::STAGE);
             }
 #pragma unroll
@@ -490,7 +521,7 @@ __global__ __launch_bounds__(NW * 64) void block_gemm_kernel(GemmArgs g) {
 // one K slice of one tile, and the fixed cost of a tile (first copies in flight, output
 // stores).
 enum GemmTile {
-    T256x256W8 = 0, T256x192W8, T256x128W8, T128x256W8, T128x192, T256x128, T128x128, T_COUNT
+    T256x256W8 = 0, T256x192W8, T256x128W8, T128x256W8, T128x192W8, T128x192, T256x128, T128x128, T_COUNT
 };
 
 struct TileInfo {
@@ -501,9 +532,10 @@ struct TileInfo {
 };
 
 static const TileInfo kTiles[T_COUNT] = {
-    {"256x256w8", 256, 256, true, false, 2.46, 14.5}, {"256x192w8", 256, 192, true, false, 2.04, 10.0},
-    {"256x128w8", 256, 128, true, false, 1.62, 5.8},  {"128x256w8", 128, 256, true, false, 1.58, 6.0},
-    {"128x192", 128, 192, true, false, 1.19, 4.4},    {"256x128", 256, 128, true, false, 1.44, 5.8},
+    {"256x256w8", 256, 256, true, false, 2.09, 14.5}, {"256x192w8", 256, 192, true, false, 2.04, 10.0},
+    {"256x128w8", 256, 128, true, true, 1.62, 5.8},   {"128x256w8", 128, 256, true, true, 1.58, 6.0},
+    {"128x192w8", 128, 192, true, true, 1.08, 4.4},   {"128x192", 128, 192, true, false, 1.21, 4.4},
+    {"256x128", 256, 128, true, false, 1.44, 5.8},
     {"128x128", 128, 128, true, true, 1.05, 3.0},
 };
 
@@ -584,7 +616,7 @@ static GemmPlan make_plan(int64_t M, int64_t N, int64_t K, bool exact, size_t ws
     const int64_t nkb = K / G_SLICE;
     GemmPlan best{T128x128, 1, (M + 127) / 128, (N + 127) / 128};
     double best_cost = 1e300;
-    const int forced_tile = exact ? -1 : env_tile(), forced_splits = exact ? 1 : env_splits();
+    const int forced_tile = env_tile(), forced_splits = exact ? 1 : env_splits();
     for (int t = 0; t < T_COUNT; ++t) {
         if (exact ? !kTiles[t].exact_ok : !kTiles[t].fp8_ok) continue;
         if (forced_tile >= 0 && t != forced_tile) continue;
@@ -634,12 +666,20 @@ hipError_t launch_block_gemm(const uint8_t *aq, const float *sa, const uint8_t *
         a.count = static_cast<uint32_t *>(workspace);
         a.part = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + kCounterBytes);
     }
-    if (exact) return launch_cfg<128, 128, 4, 2, 4, 1>(a, out_bf16, 1, stream);
+    if (exact) {
+        switch (p.tile) {
+        case T256x128W8: return launch_cfg<256, 128, 8, 4, 3, 1>(a, out_bf16, 1, stream);
+        case T128x256W8: return launch_cfg<128, 256, 8, 2, 3, 1>(a, out_bf16, 1, stream);
+        case T128x192W8: return launch_cfg<128, 192, 8, 2, 3, 1>(a, out_bf16, 1, stream);
+        default: return launch_cfg<128, 128, 4, 2, 4, 1>(a, out_bf16, 1, stream);
+        }
+    }
     switch (p.tile) {
     case T256x256W8: return launch_cfg<256, 256, 8, 2, 2, 0>(a, out_bf16, p.splits, stream);
     case T256x192W8: return launch_cfg<256, 192, 8, 2, 2, 0>(a, out_bf16, p.splits, stream);
     case T256x128W8: return launch_cfg<256, 128, 8, 4, 3, 0>(a, out_bf16, p.splits, stream);
     case T128x256W8: return launch_cfg<128, 256, 8, 2, 3, 0>(a, out_bf16, p.splits, stream);
+    case T128x192W8: return launch_cfg<128, 192, 8, 2, 3, 0>(a, out_bf16, p.splits, stream);
     case T128x192: return launch_cfg<128, 192, 4, 2, 3, 0>(a, out_bf16, p.splits, stream);
     case T256x128: return launch_cfg<256, 128, 4, 2, 3, 0>(a, out_bf16, p.splits, stream);
     default: return launch_cfg<128, 128, 4, 2, 4, 0>(a, out_bf16, p.splits, stream);

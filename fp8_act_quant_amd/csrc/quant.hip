@@ -4,6 +4,8 @@
 // training section: dynamic activation quantisation per token per 128 channels).
 // weight_quant / weight_dequant: 128x128 blocks with one fp32 scale each (same section:
 // FP8 weights in 128x128 blocks with a float32 weight_scale_inv per block).
+#include <cstdlib>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -15,13 +17,24 @@ namespace fp8q {
 // and tile t's scale is s[t] (the [M, K/128] scale grid in row-major order). One DPP row
 // (16 lanes) owns a tile: lane j holds bf16 elements 8j..8j+7 (one 16-byte load) and
 // writes their 8 codes (one 8-byte store). A wave covers 4 consecutive tiles per load
-// instruction (1 KiB contiguous) and AQ_UNROLL such groups, all loads issued before any
-// arithmetic so that AQ_UNROLL x 16 bytes per lane are in flight.
+// instruction (1 KiB contiguous); a workgroup processes groups of AQ_TILES_PER_GROUP
+// consecutive tiles, grid-stride, and issues the loads of its next group before
+// quantising the current one, so that two groups' loads per lane are in flight and the
+// stream never drains between groups.
 // ------------------------------------------------------------------------------------
 constexpr int AQ_THREADS = 256;
 constexpr int AQ_UNROLL = 4;
 constexpr int AQ_TILES_PER_WAVE = 4 * AQ_UNROLL;
-constexpr int AQ_TILES_PER_BLOCK = AQ_TILES_PER_WAVE * (AQ_THREADS / 64);
+constexpr int AQ_TILES_PER_GROUP = AQ_TILES_PER_WAVE * (AQ_THREADS / 64);
+
+__device__ __forceinline__ void aq_load(const u32x4 *__restrict__ x, int64_t tile0, int j, int64_t n_tiles,
+                                        u32x4 (&v)[AQ_UNROLL]) {
+#pragma unroll
+    for (int u = 0; u < AQ_UNROLL; ++u) {
+        const int64_t t = tile0 + 4 * u;
+        v[u] = (t < n_tiles) ? __builtin_nontemporal_load(&x[t * 16 + j]) : u32x4{0, 0, 0, 0};
+    }
+}
 
 __global__ __launch_bounds__(AQ_THREADS) void act_quant_kernel(const u32x4 *__restrict__ x,
                                                                u32x2 *__restrict__ q,
@@ -29,33 +42,52 @@ __global__ __launch_bounds__(AQ_THREADS) void act_quant_kernel(const u32x4 *__re
                                                                int64_t n_tiles) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int64_t tile0 = (int64_t)blockIdx.x * AQ_TILES_PER_BLOCK + wave * AQ_TILES_PER_WAVE + (lane >> 4);
     const int j = lane & 15;
+    const int64_t my = wave * AQ_TILES_PER_WAVE + (lane >> 4);   // this lane's first tile within a group
+    const int64_t n_groups = (n_tiles + AQ_TILES_PER_GROUP - 1) / AQ_TILES_PER_GROUP;
 
+    int64_t g = blockIdx.x;
     u32x4 v[AQ_UNROLL];
+    aq_load(x, g * AQ_TILES_PER_GROUP + my, j, n_tiles, v);
+    while (g < n_groups) {
+        const int64_t gn = g + gridDim.x;
+        u32x4 vn[AQ_UNROLL];
+        aq_load(x, gn * AQ_TILES_PER_GROUP + my, j, gn < n_groups ? n_tiles : 0, vn);
+        const int64_t tile0 = g * AQ_TILES_PER_GROUP + my;
 #pragma unroll
-    for (int u = 0; u < AQ_UNROLL; ++u) {
-        int64_t t = tile0 + 4 * u;
-        v[u] = (t < n_tiles) ? __builtin_nontemporal_load(&x[t * 16 + j]) : u32x4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int u = 0; u < AQ_UNROLL; ++u) {
-        int64_t t = tile0 + 4 * u;
-        uint32_t amax = row16_max(absmax_bits8(v[u]));
-        TileScale ts = tile_scale(amax);
-        u32x2 codes = quant8(v[u], ts);
-        if (t < n_tiles) {
-            __builtin_nontemporal_store(codes, &q[t * 16 + j]);
-            if (j == 0) s[t] = ts.s;
+        for (int u = 0; u < AQ_UNROLL; ++u) {
+            const int64_t t = tile0 + 4 * u;
+            const uint32_t amax = row16_max(absmax_bits8(v[u]));
+            const TileScale ts = tile_scale(amax);
+            const u32x2 codes = quant8(v[u], ts);
+            if (t < n_tiles) {
+                __builtin_nontemporal_store(codes, &q[t * 16 + j]);
+                if (j == 0) s[t] = ts.s;
+            }
         }
+#pragma unroll
+        for (int u = 0; u < AQ_UNROLL; ++u) v[u] = vn[u];
+        g = gn;
     }
+}
+
+// workgroups per CU of the grid-stride launch (tuning override FP8Q_AQ_WGS_PER_CU)
+static int aq_wgs_per_cu() {
+    static const int v = [] {
+        const char *e = std::getenv("FP8Q_AQ_WGS_PER_CU");
+        const int n = e ? std::atoi(e) : 0;
+        return n >= 1 && n <= 32 ? n : 16;
+    }();
+    return v;
 }
 
 hipError_t launch_act_quant(const uint16_t *x, uint8_t *q, float *s, int64_t M, int64_t K,
                             hipStream_t stream) {
     const int64_t n_tiles = M * (K / kBlock);
     if (n_tiles == 0) return hipSuccess;
-    const int64_t blocks = (n_tiles + AQ_TILES_PER_BLOCK - 1) / AQ_TILES_PER_BLOCK;
+    const int64_t groups = (n_tiles + AQ_TILES_PER_GROUP - 1) / AQ_TILES_PER_GROUP;
+    const int64_t cap = (int64_t)256 * aq_wgs_per_cu();
+    const int64_t blocks = groups < cap ? groups : cap;
     hipLaunchKernelGGL(act_quant_kernel, dim3((unsigned)blocks), dim3(AQ_THREADS), 0, stream,
                        reinterpret_cast<const u32x4 *>(x), reinterpret_cast<u32x2 *>(q), s, n_tiles);
     return hipGetLastError();
