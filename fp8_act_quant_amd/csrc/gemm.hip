@@ -32,12 +32,14 @@
 // Schedule of one slice, per wave. The W fragments of the slice and the A fragment of the
 // first 16-row group are in registers when it starts. For each row group i the A
 // fragment of group i+1 is read, the SUB_N MFMAs of group i are issued, and between them
-// the promotion FMAs of group i-1 (whose MFMAs have finished by then); scheduling barriers
-// keep the compiler from regrouping these. After the last group's MFMAs are issued the
-// wave waits for its share of the next slice's copies, meets the other waves at the
-// workgroup barrier (after which the finished slice's buffer is free), queues the copies
-// of slice kb + NSTAGE into that buffer, reads the next slice's first fragments, and only
-// then promotes the last group: the matrix unit stays busy across the barrier.
+// go the promotion FMAs of the previous group (whose MFMAs have finished by then; the last
+// group of a slice is promoted during the first group of the next) and a few of the copy
+// instructions of slice kb + NSTAGE - 1. Scheduling barriers keep the compiler from
+// regrouping these. Once per slice the wave waits for its share of the next slice's
+// copies and meets the other waves at the workgroup barrier, after which the next slice is
+// visible and the buffer of slice kb - 1 (now refilled during slice kb + 1) is free; then
+// it reads the next slice's first fragments while MFMAs it has already issued keep the
+// matrix unit busy.
 //
 // Split-K. For shapes with too few tiles to fill the 256 CUs the K slices are divided into
 // `splits` contiguous ranges. Each workgroup stores its fp32 partial tile to the caller's
@@ -142,6 +144,9 @@ __device__ __forceinline__ void promote(f32x4 &acc, const f32x4 &p, float f) {
     for (int r = 0; r < 4; ++r) acc[r] = __builtin_fmaf(p[r], f, acc[r]);
     asm volatile("" : "+v"(acc));
 }
+
+// wait for every outstanding LDS read (lgkmcnt 0; vmcnt and expcnt left alone)
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14)); }
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -257,7 +262,8 @@ struct DmaPlan {
 
     // all copies of slice kb into stage buffer `base`
     __device__ __forceinline__ void issue(uint8_t *base, int64_t kb) const {
-        const int koff = (int)(kb * G_SLICE), soff = (int)(kb * 4);
+        const int koff = __builtin_amdgcn_readfirstlane((int)(kb * G_SLICE));
+        const int soff = __builtin_amdgcn_readfirstlane((int)(kb * 4));
 #pragma unroll
         for (int I = 0; I < S::IPW; ++I) issue_one(base, koff, soff, I);
     }
@@ -267,7 +273,10 @@ struct DmaPlan {
     template <int NG>
     __device__ __forceinline__ void issue_part(uint8_t *base, int64_t kb, int g) const {
         constexpr int PER = (S::IPW + NG - 1) / NG;
-        const int koff = (int)(kb * G_SLICE), soff = (int)(kb * 4);
+        // kb is the same in every lane; saying so keeps the offsets in SGPRs (a VGPR soffset
+        // would make the compiler wrap each copy in a per-value loop)
+        const int koff = __builtin_amdgcn_readfirstlane((int)(kb * G_SLICE));
+        const int soff = __builtin_amdgcn_readfirstlane((int)(kb * 4));
 #pragma unroll
         for (int c = 0; c < PER; ++c)
             if (g * PER + c < S::IPW) issue_one(base, koff, soff, g * PER + c);
@@ -373,12 +382,27 @@ __global__ __launch_bounds__(NW * 64) void block_gemm_kernel(GemmArgs g) {
         };
         load_slice_head(smem);
 
+        // Where the slice barrier sits. With three or more stages the copies have slack, and
+        // the barrier goes before the last row group: that group's MFMAs (operands already in
+        // registers) then run while the next slice's first fragments are read. With two
+        // stages the next slice's copies have only one slice of lead, and the barrier goes
+        // after the last group's MFMAs, as late as possible (measured: 4% faster there).
+        constexpr bool EARLY_BARRIER = NSTAGE >= 3;
+        // promotion of each row group runs one group behind its MFMAs (the last group of a
+        // slice is promoted during the first group of the next); it starts from a zero partial
         f32x4 p_prev[SUB_N];
         float f_prev[SUB_N];
+#pragma unroll
+        for (int j = 0; j < SUB_N; ++j) {
+            p_prev[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            f_prev[j] = 0.f;
+        }
         int st = 0;
         for (int64_t kb = kb0; kb < kb1; ++kb) {
             const uint8_t *stage = smem + st * S::STAGE;
             const float *tS = reinterpret_cast<const float *>(stage + S::A_BYTES + S::W_BYTES);
+            const int st_next = st + 1 == NSTAGE ? 0 : st + 1;
+            const bool more = kb + 1 < kb1;
             // the copies of slice kb + NSTAGE - 1 go into the buffer of slice kb - 1, free since
             // the barrier that ended slice kb - 1; they are spread over this slice's row groups
             // so that the matrix unit is never left waiting behind a burst of copy issues
@@ -386,6 +410,13 @@ __global__ __launch_bounds__(NW * 64) void block_gemm_kernel(GemmArgs g) {
             uint8_t *const copy_dst = smem + (st == 0 ? NSTAGE - 1 : st - 1) * S::STAGE;
 #pragma unroll
             for (int i = 0; i < SUB_M; ++i) {
+                if (EARLY_BARRIER && i == SUB_M - 1 && more) {
+                    // every LDS read of slice kb is done (the last group's operands are in
+                    // registers); once all waves are past the barrier the next slice has landed
+                    wait_lgkm0();
+                    wait_slice<S::IPW, NSTAGE - 2>((int)min64(NSTAGE - 2, kb1 - 1 - (kb + 1)));
+                    lds_barrier();
+                }
                 i32x8 af_n = af;
                 float sav_n = sav;
                 if (i + 1 < SUB_M) {
@@ -396,13 +427,14 @@ __global__ __launch_bounds__(NW * 64) void block_gemm_kernel(GemmArgs g) {
 #pragma unroll
                 for (int j = 0; j < SUB_N; ++j) f_cur[j] = sav * (ONE_SW ? swv[0] : swv[j]);
                 f32x4 p_cur[SUB_N];
+                const int ip = i == 0 ? SUB_M - 1 : i - 1;   // row group being promoted (a constant once unrolled)
                 if constexpr (EXACT) {
                     const Frag16 ah = to_f16(af);
 #pragma unroll
                     for (int j = 0; j < SUB_N; ++j) {
                         p_cur[j] = mfma_slice_exact(wh[j], ah);
                         if (j == 0 && copy_now) dma.template issue_part<SUB_M>(copy_dst, kb + NSTAGE - 1, i);
-                        if (i > 0) promote(acc[i - 1][j], p_prev[j], f_prev[j]);
+                        promote(acc[ip][j], p_prev[j], f_prev[j]);
                         __builtin_amdgcn_sched_barrier(0);
                     }
                 } else {
@@ -410,30 +442,33 @@ __global__ __launch_bounds__(NW * 64) void block_gemm_kernel(GemmArgs g) {
                     for (int j = 0; j < SUB_N; ++j) {
                         p_cur[j] = mfma_slice(wf[j], af);
                         if (j == 0 && copy_now) dma.template issue_part<SUB_M>(copy_dst, kb + NSTAGE - 1, i);
-                        if (i > 0) promote(acc[i - 1][j], p_prev[j], f_prev[j]);
+                        promote(acc[ip][j], p_prev[j], f_prev[j]);
                         __builtin_amdgcn_sched_barrier(0);
                     }
+                }
+                // the last group's MFMAs have taken their operands: the next slice's first
+                // fragments load while they run
+                if (i == SUB_M - 1 && more) {
+                    if (!EARLY_BARRIER) {
+                        wait_slice<S::IPW, NSTAGE - 2>((int)min64(NSTAGE - 2, kb1 - 1 - (kb + 1)));
+                        lds_barrier();
+                    }
+                    load_slice_head(smem + st_next * S::STAGE);
                 }
 #pragma unroll
                 for (int j = 0; j < SUB_N; ++j) {
                     p_prev[j] = p_cur[j];
                     f_prev[j] = f_cur[j];
                 }
-                af = af_n;
-                sav = sav_n;
+                if (i + 1 < SUB_M) {
+                    af = af_n;
+                    sav = sav_n;
+                }
             }
-            // the last group's MFMAs are in flight: move on to the next slice meanwhile
-            const int st_next = st + 1 == NSTAGE ? 0 : st + 1;
-            if (kb + 1 < kb1) {
-                wait_slice<S::IPW, NSTAGE - 2>((int)min64(NSTAGE - 2, kb1 - 1 - (kb + 1)));
-                lds_barrier();
-                load_slice_head(smem + st_next * S::STAGE);
-            }
-#pragma unroll
-            for (int j = 0; j < SUB_N; ++j) promote(acc[SUB_M - 1][j], p_prev[j], f_prev[j]);
-            __builtin_amdgcn_sched_barrier(0);
             st = st_next;
         }
+#pragma unroll
+        for (int j = 0; j < SUB_N; ++j) promote(acc[SUB_M - 1][j], p_prev[j], f_prev[j]);
     }
 
     if (g.splits > 1) {
@@ -465,20 +500,24 @@ __global__ __launch_bounds__(NW * 64) void block_gemm_kernel(GemmArgs g) {
         __syncthreads();
         if (!*flag) return;
         // the last to arrive sums the partials in split order (independent of which split
-        // arrived last), one 16x16 block at a time, with device-coherent loads
+        // arrived last), one row group at a time; its own partial is read back like the
+        // others (the loads of a row group are all issued before the first is needed)
 #pragma unroll
-        for (int i = 0; i < SUB_M; ++i)
+        for (int i = 0; i < SUB_M; ++i) {
+            f32x4 t[SUB_N];
+            for (int sp = 0; sp < g.splits; ++sp) {
+                f32x4 v[SUB_N];
 #pragma unroll
-            for (int j = 0; j < SUB_N; ++j) {
-                const uint32_t o = lane_off + (i * SUB_N + j) * 1024;
-                f32x4 t = split == 0 ? acc[i][j]
-                                     : __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rp, o, 0, kDeviceScope));
-                for (int sp = 1; sp < g.splits; ++sp)
-                    t += sp == split ? acc[i][j]
-                                     : __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                                     rp, o, sp * (BM * BN * 4), kDeviceScope));
-                acc[i][j] = t;
+                for (int j = 0; j < SUB_N; ++j)
+                    v[j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                         rp, lane_off + (i * SUB_N + j) * 1024, sp * (BM * BN * 4),
+                                                         kDeviceScope));
+#pragma unroll
+                for (int j = 0; j < SUB_N; ++j) t[j] = sp == 0 ? v[j] : t[j] + v[j];
             }
+#pragma unroll
+            for (int j = 0; j < SUB_N; ++j) acc[i][j] = t[j];
+        }
     }
 
     // epilogue: lane holds Y[m][n .. n+3] for each (i, j)
