@@ -520,32 +520,64 @@ __global__ __launch_bounds__(NW * 64) void block_gemm_kernel(GemmArgs g) {
         }
     }
 
-    // epilogue: lane holds Y[m][n .. n+3] for each (i, j)
-    const bool vec_ok = (N & 3) == 0;
+    // Epilogue, staged through LDS (the stage buffers are free once every wave is past the
+    // K loop): the fragments of IPR row groups are written to LDS as output rows, then the
+    // workgroup stores them with 16 bytes per lane, so that every store instruction writes
+    // whole 128-byte pieces of output rows. The LDS row stride is padded so that both the
+    // fragment writes (16 rows x 4 column groups per instruction) and the row reads are
+    // free of bank conflicts.
+    {
+        constexpr int OB = OUT_BF16 ? 2 : 4;                 // bytes per output element
+        constexpr int EPC = 16 / OB;                         // elements per 16-byte chunk
+        constexpr int ROW_WORDS = BN * OB / 4;
+        constexpr int TARGET = OUT_BF16 ? 8 : 16;            // row stride, in banks, mod 64
+        constexpr int LDS_ROW = 4 * (ROW_WORDS + ((TARGET - ROW_WORDS) % 64 + 64) % 64);
+        constexpr int RG = WAVES_M * 16;                     // tile rows of one row-group index
+        constexpr int IPR0 = (S::STAGE * NSTAGE) / (RG * LDS_ROW);
+        constexpr int IPR = IPR0 < SUB_M ? IPR0 : SUB_M;     // row groups per round
+        static_assert(IPR >= 1, "epilogue staging does not fit");
+        constexpr int CPR = BN * OB / 16;                    // 16-byte chunks per output row
+        const bool vec_ok = ((N * OB) & 15) == 0;            // every output row 16-byte aligned
 #pragma unroll
-    for (int i = 0; i < SUB_M; ++i) {
-        const int64_t m = m0 + wm * WM + 16 * i + frow;
-        if (m >= M) continue;
+        for (int i0 = 0; i0 < SUB_M; i0 += IPR) {
+            __syncthreads();
 #pragma unroll
-        for (int j = 0; j < SUB_N; ++j) {
-            const int64_t n = n0 + wn * WN + 16 * j + 4 * kgroup;
-            if (n >= N) continue;
-            const f32x4 v = acc[i][j];
-            if constexpr (OUT_BF16) {
-                uint16_t *yp = reinterpret_cast<uint16_t *>(g.y) + m * N + n;
-                const uint32_t lo = pack_bf16x2(v[0], v[1]), hi = pack_bf16x2(v[2], v[3]);
-                if (vec_ok && n + 3 < N) {
-                    *reinterpret_cast<u32x2 *>(yp) = u32x2{lo, hi};
-                } else {
-                    const uint16_t h[4] = {(uint16_t)lo, (uint16_t)(lo >> 16), (uint16_t)hi, (uint16_t)(hi >> 16)};
-                    for (int r = 0; r < 4 && n + r < N; ++r) yp[r] = h[r];
+            for (int ii = 0; ii < IPR; ++ii) {
+                const int i = i0 + ii;
+                if (i < SUB_M) {
+                    uint8_t *rowp = smem + (ii * RG + wm * 16 + frow) * LDS_ROW;
+#pragma unroll
+                    for (int j = 0; j < SUB_N; ++j) {
+                        const int col = wn * WN + 16 * j + 4 * kgroup;
+                        const f32x4 v = acc[i][j];
+                        if constexpr (OUT_BF16)
+                            *reinterpret_cast<u32x2 *>(rowp + col * 2) =
+                                u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+                        else
+                            *reinterpret_cast<f32x4 *>(rowp + col * 4) = v;
+                    }
                 }
-            } else {
-                float *yp = reinterpret_cast<float *>(g.y) + m * N + n;
-                if (vec_ok && n + 3 < N) {
-                    *reinterpret_cast<f32x4 *>(yp) = v;
+            }
+            __syncthreads();
+            const int groups = (SUB_M - i0) < IPR ? (SUB_M - i0) : IPR;
+            const int chunks = groups * RG * CPR;
+            for (int c = threadIdx.x; c < chunks; c += NW * 64) {
+                const int r = c / CPR, cb = c - r * CPR;
+                const int ii = r / RG, within = r - ii * RG;
+                const int64_t m = m0 + (within >> 4) * WM + 16 * (i0 + ii) + (within & 15);
+                const int64_t n = n0 + cb * EPC;
+                if (m >= M || n >= N) continue;
+                const uint8_t *src = smem + r * LDS_ROW + cb * 16;
+                uint8_t *yp = reinterpret_cast<uint8_t *>(g.y) + (m * N + n) * OB;
+                if (vec_ok && n + EPC <= N) {
+                    __builtin_nontemporal_store(*reinterpret_cast<const u32x4 *>(src), reinterpret_cast<u32x4 *>(yp));
                 } else {
-                    for (int r = 0; r < 4 && n + r < N; ++r) yp[r] = v[r];
+                    for (int e = 0; e < EPC && n + e < N; ++e) {
+                        if constexpr (OUT_BF16)
+                            reinterpret_cast<uint16_t *>(yp)[e] = reinterpret_cast<const uint16_t *>(src)[e];
+                        else
+                            reinterpret_cast<float *>(yp)[e] = reinterpret_cast<const float *>(src)[e];
+                    }
                 }
             }
         }
@@ -560,7 +592,8 @@ __global__ __launch_bounds__(NW * 64) void block_gemm_kernel(GemmArgs g) {
 // one K slice of one tile, and the fixed cost of a tile (first copies in flight, output
 // stores).
 enum GemmTile {
-    T256x256W8 = 0, T256x192W8, T256x128W8, T128x256W8, T128x192W8, T128x192, T256x128, T128x128, T_COUNT
+    T256x256W8 = 0, T256x192W8, T256x128W8, T128x256W8, T128x192W8, T128x192, T256x128, T128x128, T128x128S2,
+    T_COUNT
 };
 
 struct TileInfo {
@@ -575,7 +608,7 @@ static const TileInfo kTiles[T_COUNT] = {
     {"256x128w8", 256, 128, true, true, 1.62, 5.8},   {"128x256w8", 128, 256, true, true, 1.58, 6.0},
     {"128x192w8", 128, 192, true, true, 1.08, 4.4},   {"128x192", 128, 192, true, false, 1.21, 4.4},
     {"256x128", 256, 128, true, false, 1.44, 5.8},
-    {"128x128", 128, 128, true, true, 1.05, 3.0},
+    {"128x128", 128, 128, true, true, 1.05, 3.0},     {"128x128s2", 128, 128, false, false, 1.05, 3.0},
 };
 
 constexpr int kNumCUs = 256;
@@ -657,8 +690,8 @@ static GemmPlan make_plan(int64_t M, int64_t N, int64_t K, bool exact, size_t ws
     double best_cost = 1e300;
     const int forced_tile = env_tile(), forced_splits = exact ? 1 : env_splits();
     for (int t = 0; t < T_COUNT; ++t) {
-        if (exact ? !kTiles[t].exact_ok : !kTiles[t].fp8_ok) continue;
-        if (forced_tile >= 0 && t != forced_tile) continue;
+        // a forced tile (tuning) is taken even where the planner would not pick it
+        if (forced_tile >= 0 ? t != forced_tile : (exact ? !kTiles[t].exact_ok : !kTiles[t].fp8_ok)) continue;
         const int64_t tm = (M + kTiles[t].bm - 1) / kTiles[t].bm, tn = (N + kTiles[t].bn - 1) / kTiles[t].bn;
         for (int s = 1; s <= (exact ? 1 : kMaxSplits); ++s) {
             // a split contracts at least 2 slices; a forced count falls back to 1 where it cannot apply
@@ -721,6 +754,7 @@ hipError_t launch_block_gemm(const uint8_t *aq, const float *sa, const uint8_t *
     case T128x192W8: return launch_cfg<128, 192, 8, 2, 3, 0>(a, out_bf16, p.splits, stream);
     case T128x192: return launch_cfg<128, 192, 4, 2, 3, 0>(a, out_bf16, p.splits, stream);
     case T256x128: return launch_cfg<256, 128, 4, 2, 3, 0>(a, out_bf16, p.splits, stream);
+    case T128x128S2: return launch_cfg<128, 128, 4, 2, 2, 0>(a, out_bf16, p.splits, stream);
     default: return launch_cfg<128, 128, 4, 2, 4, 0>(a, out_bf16, p.splits, stream);
     }
 }
