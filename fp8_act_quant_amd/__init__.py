@@ -22,7 +22,7 @@ from ._lib import (FP8Q_GEMM_EXACT_SLICES, FP8Q_GEMM_FP8_PRODUCTS, FP8Q_OUT_BF16
 BLOCK = 128
 
 __all__ = [
-    "BLOCK", "Fp8qError", "act_quant", "weight_quant", "weight_dequant", "fp8_gemm",
+    "BLOCK", "Fp8qError", "act_quant", "weight_quant", "weight_dequant", "fp8_gemm", "linear",
     "gemm_workspace_bytes", "lib",
 ]
 
@@ -129,7 +129,7 @@ def _auto_workspace(device: torch.device, stream: int, nbytes: int) -> torch.Ten
 
 def fp8_gemm(a: torch.Tensor, a_s: torch.Tensor, w: torch.Tensor, w_s: torch.Tensor,
              out_dtype=torch.bfloat16, workspace="auto", out: torch.Tensor | None = None,
-             mode: str = "default") -> torch.Tensor:
+             mode: str = "default", bias: torch.Tensor | None = None) -> torch.Tensor:
     """Block-scaled Y = A . W^T. a: float8_e4m3fn [..., K] with scales [..., K/128];
     w: float8_e4m3fn [N, K] with scales [ceil(N/128), K/128]. Returns [..., N] in
     out_dtype (torch.float32 or torch.bfloat16).
@@ -139,7 +139,9 @@ def fp8_gemm(a: torch.Tensor, a_s: torch.Tensor, w: torch.Tensor, w_s: torch.Ten
     output and "fp8" for bfloat16 output.
 
     workspace: "auto" (a zero-initialised workspace cached per device and stream), None
-    (no split-K), or a uint8 tensor that was zero-filled before its first use."""
+    (no split-K), or a uint8 tensor that was zero-filled before its first use.
+
+    bias: optional [N] vector, added in fp32 to every row before the output rounding."""
     if mode not in _MODES:
         raise ValueError(f"mode must be one of {sorted(_MODES)}")
     _need(a, "a", torch.float8_e4m3fn)
@@ -178,8 +180,37 @@ def fp8_gemm(a: torch.Tensor, a_s: torch.Tensor, w: torch.Tensor, w_s: torch.Ten
     elif workspace is not None:
         _need(workspace, "workspace", workspace.dtype)
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    b_ptr = None
+    if bias is not None:
+        if not isinstance(bias, torch.Tensor) or bias.device != a.device or tuple(bias.shape) != (N,):
+            raise ValueError(f"bias must be a [{N}] tensor on {a.device}")
+        bias = bias.to(torch.float32).contiguous()
+        b_ptr = bias.data_ptr()
     with torch.cuda.device(a.device):
-        check("fp8_block_gemm", lib.fp8_block_gemm(a.data_ptr(), a_s.data_ptr(), w.data_ptr(), w_s.data_ptr(),
-                                                   out.data_ptr(), code, M, N, K, ws_ptr or None, ws_bytes,
-                                                   _stream(a)))
+        check("fp8_block_gemm_bias", lib.fp8_block_gemm_bias(a.data_ptr(), a_s.data_ptr(), w.data_ptr(),
+                                                             w_s.data_ptr(), b_ptr, out.data_ptr(), code, M, N, K,
+                                                             ws_ptr or None, ws_bytes, _stream(a)))
     return out
+
+
+def linear(x: torch.Tensor, weight: torch.Tensor, bias: torch.Tensor | None = None,
+           weight_scale: torch.Tensor | None = None, gemm_impl: str = "fp8",
+           out_dtype=torch.bfloat16) -> torch.Tensor:
+    """The linear() dispatch of the pomoai.com "DeepSeek-V3" page (FP8 mixed-precision
+    training section): a weight stored in more than one byte per element is applied as is
+    (torch's linear); with gemm_impl == "bf16" the FP8 weight is dequantised with
+    weight_dequant and applied by torch's linear; otherwise x is quantised with act_quant
+    and multiplied by fp8_gemm, with the bias added in the GEMM's epilogue.
+
+    x: bf16 [..., K]; weight: [N, K] (float8_e4m3fn with weight_scale
+    [ceil(N/128), K/128], or a wider dtype); bias: optional [N]."""
+    if weight.element_size() > 1:
+        return torch.nn.functional.linear(x, weight, bias)
+    if weight_scale is None:
+        raise ValueError("an FP8 weight needs its weight_scale")
+    if gemm_impl == "bf16":
+        return torch.nn.functional.linear(x, weight_dequant(weight, weight_scale), bias)
+    if gemm_impl != "fp8":
+        raise ValueError('gemm_impl must be "fp8" or "bf16"')
+    q, s = act_quant(x)
+    return fp8_gemm(q, s, weight, weight_scale, out_dtype=out_dtype, bias=bias)

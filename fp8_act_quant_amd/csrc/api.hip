@@ -81,6 +81,12 @@ int fp8_weight_dequant(const uint8_t *q, const float *s, uint16_t *w, int64_t N,
 int fp8_block_gemm(const uint8_t *aq, const float *sa, const uint8_t *wq, const float *sw, void *y,
                    int y_dtype, int64_t M, int64_t N, int64_t K, void *workspace, size_t workspace_bytes,
                    void *stream) {
+    return fp8_block_gemm_bias(aq, sa, wq, sw, nullptr, y, y_dtype, M, N, K, workspace, workspace_bytes, stream);
+}
+
+int fp8_block_gemm_bias(const uint8_t *aq, const float *sa, const uint8_t *wq, const float *sw, const float *bias,
+                        void *y, int y_dtype, int64_t M, int64_t N, int64_t K, void *workspace,
+                        size_t workspace_bytes, void *stream) {
     const int dtype = y_dtype & 0xFF;
     const int mode = y_dtype & ~0xFF;
     if (dtype != FP8Q_OUT_F32 && dtype != FP8Q_OUT_BF16) return FP8Q_ERR_DTYPE;
@@ -93,15 +99,15 @@ int fp8_block_gemm(const uint8_t *aq, const float *sa, const uint8_t *wq, const 
     if (!y) return FP8Q_ERR_NULL;
     if (K > 0 && (!aq || !sa || !wq || !sw)) return FP8Q_ERR_NULL;
     if (misaligned(aq, 16) || misaligned(wq, 16) || misaligned(y, 16) || misaligned(sa, 4) ||
-        misaligned(sw, 4))
+        misaligned(sw, 4) || misaligned(bias, 4))
         return FP8Q_ERR_ALIGN;
     if (workspace == nullptr) workspace_bytes = 0;
     if (workspace_bytes && misaligned(workspace, 16)) return FP8Q_ERR_ALIGN;
     if (int e = check_device()) return e;
     // default contraction: exact slices for fp32 output, the FP8 matrix unit for bf16 output
     const bool exact = mode == FP8Q_GEMM_EXACT_SLICES || (mode == 0 && dtype == FP8Q_OUT_F32);
-    return finish(fp8q::launch_block_gemm(aq, sa, wq, sw, y, dtype == FP8Q_OUT_BF16, exact, M, N, K, workspace,
-                                          workspace_bytes, static_cast<hipStream_t>(stream)));
+    return finish(fp8q::launch_block_gemm(aq, sa, wq, sw, bias, y, dtype == FP8Q_OUT_BF16, exact, M, N, K,
+                                          workspace, workspace_bytes, static_cast<hipStream_t>(stream)));
 }
 
 size_t fp8_block_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int y_dtype) {
@@ -128,6 +134,6 @@ const char *fp8q_strerror(int status) {
     }
 }
 
-int fp8q_version(void) { return (1 << 16) | 0; }
+int fp8q_version(void) { return (1 << 16) | 1; }
 
 }  // extern "C"

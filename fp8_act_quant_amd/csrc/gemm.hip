@@ -290,6 +290,7 @@ struct GemmArgs {
     const uint8_t *wq;
     const float *sw;
     void *y;
+    const float *bias;  // [N] fp32 added to every row before the output rounding, or null
     float *part;        // split-K partial tiles [splits][tiles][BM * BN], or null
     uint32_t *count;    // split-K arrival counter per tile, zero between calls
     int64_t M, N, K;
@@ -538,6 +539,18 @@ __global__ __launch_bounds__(NW * 64) void block_gemm_kernel(GemmArgs g) {
         static_assert(IPR >= 1, "epilogue staging does not fit");
         constexpr int CPR = BN * OB / 16;                    // 16-byte chunks per output row
         const bool vec_ok = ((N * OB) & 15) == 0;            // every output row 16-byte aligned
+        // bias of this lane's four output columns of each n-subtile (zero past N)
+        f32x4 bvec[SUB_N];
+#pragma unroll
+        for (int j = 0; j < SUB_N; ++j) {
+            bvec[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (g.bias) {
+                const int64_t n = n0 + wn * WN + 16 * j + 4 * kgroup;
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (n + r < N) bvec[j][r] = g.bias[n + r];
+            }
+        }
 #pragma unroll
         for (int i0 = 0; i0 < SUB_M; i0 += IPR) {
             __syncthreads();
@@ -549,7 +562,7 @@ __global__ __launch_bounds__(NW * 64) void block_gemm_kernel(GemmArgs g) {
 #pragma unroll
                     for (int j = 0; j < SUB_N; ++j) {
                         const int col = wn * WN + 16 * j + 4 * kgroup;
-                        const f32x4 v = acc[i][j];
+                        const f32x4 v = acc[i][j] + bvec[j];
                         if constexpr (OUT_BF16)
                             *reinterpret_cast<u32x2 *>(rowp + col * 2) =
                                 u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
@@ -729,11 +742,11 @@ static hipError_t launch_cfg(GemmArgs a, bool out_bf16, int splits, hipStream_t 
 }
 
 hipError_t launch_block_gemm(const uint8_t *aq, const float *sa, const uint8_t *wq, const float *sw,
-                             void *y, bool out_bf16, bool exact, int64_t M, int64_t N, int64_t K, void *workspace,
-                             size_t workspace_bytes, hipStream_t stream) {
+                             const float *bias, void *y, bool out_bf16, bool exact, int64_t M, int64_t N, int64_t K,
+                             void *workspace, size_t workspace_bytes, hipStream_t stream) {
     if (M == 0 || N == 0) return hipSuccess;
     const GemmPlan p = make_plan(M, N, K, exact, workspace ? workspace_bytes : 0, false);
-    GemmArgs a{aq, sa, wq, sw, y, nullptr, nullptr, M, N, K, 0, 0, 1, 1};
+    GemmArgs a{aq, sa, wq, sw, y, bias, nullptr, nullptr, M, N, K, 0, 0, 1, 1};
     if (p.splits > 1) {
         a.count = static_cast<uint32_t *>(workspace);
         a.part = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + kCounterBytes);

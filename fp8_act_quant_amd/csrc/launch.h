@@ -17,12 +17,12 @@ hipError_t launch_weight_dequant(const uint8_t *q, const float *s, uint16_t *w, 
 
 // Block-scaled GEMM. out_bf16 selects the output dtype; exact selects the exact-slice
 // contraction (f16 matrix unit on exactly converted operands) instead of the FP8 matrix
-// unit. The workspace (may be NULL) is used for a split-K schedule when workspace_bytes >=
+// unit. bias (fp32 [N], may be NULL) is added in fp32 before the output rounding. The workspace (may be NULL) is used for a split-K schedule when workspace_bytes >=
 // gemm_workspace_bytes(M, N, K, out_bf16, exact); it must hold zeros in its counter area
 // before its first use, and every call leaves them zero.
 hipError_t launch_block_gemm(const uint8_t *aq, const float *sa, const uint8_t *wq, const float *sw,
-                             void *y, bool out_bf16, bool exact, int64_t M, int64_t N, int64_t K,
-                             void *workspace, size_t workspace_bytes, hipStream_t stream);
+                             const float *bias, void *y, bool out_bf16, bool exact, int64_t M, int64_t N,
+                             int64_t K, void *workspace, size_t workspace_bytes, hipStream_t stream);
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, bool out_bf16, bool exact);
 
 }  // namespace fp8q

@@ -132,6 +132,18 @@ int fp8_block_gemm(const uint8_t *aq, const float *sa, const uint8_t *wq, const 
                    void *y, int y_dtype, int64_t M, int64_t N, int64_t K, void *workspace,
                    size_t workspace_bytes, void *stream);
 
+/* fp8_block_gemm_bias -- fp8_block_gemm with a bias row added to the output.
+ * (pomoai.com "DeepSeek-V3", the FP8 branch of linear(): y = fp8_gemm(...), then
+ * y += bias when a bias is given.)
+ *   bias [N] fp32 (4-byte aligned), or NULL for no bias. It is added to the fp32
+ *   accumulator of every row before the output rounding, so a bf16 output is rounded once:
+ *   Y[m, n] = RN_out(acc[m, n] + bias[n]).
+ *   All other arguments, and the behaviour, are those of fp8_block_gemm (which is this
+ *   call with bias = NULL). */
+int fp8_block_gemm_bias(const uint8_t *aq, const float *sa, const uint8_t *wq, const float *sw,
+                        const float *bias, void *y, int y_dtype, int64_t M, int64_t N, int64_t K,
+                        void *workspace, size_t workspace_bytes, void *stream);
+
 /* Workspace size in bytes that lets fp8_block_gemm use its split-K schedule for this
  * shape and y_dtype (including the mode bits); 0 if that call does not use one or the
  * arguments are invalid. Host-only; enqueues nothing. */

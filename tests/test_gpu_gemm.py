@@ -224,6 +224,59 @@ def test_gemm_split_k_workspace(M, N, K):
     assert np.all(d <= 2.0 ** -17 * bound + 1e-30), float(np.max(d / np.maximum(bound, 1e-300)))
 
 
+@pytest.mark.parametrize("mode", ["exact", "fp8"])
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+@pytest.mark.parametrize("M,N,K", [(300, 576, 2048), (129, 200, 384), (64, 256, 256)])
+def test_gemm_bias_epilogue(M, N, K, out, mode):
+    """Bias added in fp32 before the output rounding: against the oracle's y_hat + bias
+    (float64), with the one extra fp32 rounding of the addition allowed (2^-23 |y_hat + b|);
+    a bf16 output must be within 1 ulp of RN_bf16(y_hat + b). Split-K shapes included."""
+    A = synth.random_bf16((M, K), seed=5 * M + K)
+    W = synth.random_bf16((N, K), seed=9 * N + K, std=0.02)
+    bias = np.random.Generator(np.random.PCG64(N)).standard_normal(N).astype(np.float32)
+    aq, sa, wq, sw = quantise_on_gpu(A, W)
+    b = torch.from_numpy(bias).cuda()
+    y = fq.fp8_gemm(aq, sa, wq, sw, out_dtype=TORCH_OUT[out], mode=mode, bias=b)
+    y0 = fq.fp8_gemm(aq, sa, wq, sw, out_dtype=TORCH_OUT[out], mode=mode)
+    y0b = fq.fp8_gemm(aq, sa, wq, sw, out_dtype=TORCH_OUT[out], mode=mode, bias=torch.zeros_like(b))
+    torch.cuda.synchronize()
+    assert torch.equal(y0.view(torch.int16 if out == "bf16" else torch.int32),
+                       y0b.view(torch.int16 if out == "bf16" else torch.int32)), "a zero bias changed the output"
+    haq, hsa, hwq, hsw = host_codes(aq), sa.cpu().numpy(), host_codes(wq), sw.cpu().numpy()
+    y_hat, bound = oracle.block_gemm(haq, hsa, hwq, hsw)
+    y_hat_b = y_hat + bias.astype(np.float64)[None, :]
+    rows, cols = np.repeat(np.arange(M), N), np.tile(np.arange(N), M)
+    allowance = scale_floor(haq, hwq, rows, cols).reshape(M, N) + 2.0 ** -23 * np.abs(y_hat_b)
+    if mode == "fp8":
+        allowance = allowance + mfma_group_allowance(haq, hsa, hwq, hsw, rows, cols).reshape(M, N)
+    res = gemm_check(y_host(y, out), y_hat_b, bound, out, allowance)
+    print(f"bias {M}x{N}x{K} {out} {mode}", res, flush=True)
+    assert res["violations"] == 0, res
+
+
+def test_linear_dispatch():
+    """linear(): the FP8 branch is act_quant + fp8_gemm with the bias fused; the bf16
+    branch dequantises the weight and applies torch's linear; a bf16 weight is used as is."""
+    M, N, K = 37, 300, 512
+    x = dev_bf16(synth.random_bf16((M, K), seed=41))
+    Wb = dev_bf16(synth.random_bf16((N, K), seed=42, std=0.02))
+    bias = dev_bf16(synth.random_bf16((N,), seed=43))
+    wq, sw = fq.weight_quant(Wb)
+    q, s = fq.act_quant(x)
+    ref_fp8 = fq.fp8_gemm(q, s, wq, sw, out_dtype=torch.bfloat16, bias=bias)
+    y_fp8 = fq.linear(x, wq, bias, weight_scale=sw)
+    assert torch.equal(y_fp8.view(torch.int16), ref_fp8.view(torch.int16))
+    y_bf16 = fq.linear(x, wq, bias, weight_scale=sw, gemm_impl="bf16")
+    ref_bf16 = torch.nn.functional.linear(x, fq.weight_dequant(wq, sw), bias)
+    assert torch.equal(y_bf16.view(torch.int16), ref_bf16.view(torch.int16))
+    y_pass = fq.linear(x, Wb, bias)
+    assert torch.equal(y_pass.view(torch.int16), torch.nn.functional.linear(x, Wb, bias).view(torch.int16))
+    with pytest.raises(ValueError):
+        fq.linear(x, wq, bias)   # FP8 weight without its scale
+    with pytest.raises(ValueError):
+        fq.fp8_gemm(q, s, wq, sw, bias=bias[:-1])
+
+
 @pytest.mark.parametrize("name", ["q_down", "kv_down", "kv_up", "outlier"])
 def test_gemm_workload_full_size_sampled(name):
     wl = synth.WORKLOADS[name]
