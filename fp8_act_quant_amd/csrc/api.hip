@@ -121,6 +121,12 @@ size_t fp8_block_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int y_dty
     return fp8q::gemm_workspace_bytes(M, N, K, dtype == FP8Q_OUT_BF16, exact);
 }
 
+int fp8q_gemm_force_config(int config, int splits) {
+    return fp8q::gemm_force_config(config, splits) ? FP8Q_OK : FP8Q_ERR_SHAPE;
+}
+
+const char *fp8q_gemm_config_name(int config) { return fp8q::gemm_config_name(config); }
+
 const char *fp8q_strerror(int status) {
     switch (status) {
     case FP8Q_OK: return "ok";

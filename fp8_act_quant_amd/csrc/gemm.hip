@@ -46,6 +46,7 @@
 // workspace and bumps the tile's arrival counter; the last to arrive adds the partials in
 // split order (so the result does not depend on arrival order), writes Y and resets the
 // counter to zero.
+#include <atomic>
 #include <cstdlib>
 #include <cstring>
 
@@ -654,25 +655,45 @@ struct GemmPlan {
     int64_t tiles_m, tiles_n;
 };
 
-// Tuning overrides, read once: FP8Q_GEMM_TILE (a tile name) and FP8Q_GEMM_SPLITS.
+// Forced configuration for tuning and tests: a tile index (or -1 for the planner's
+// choice) and a split count (or 0). Initialised from FP8Q_GEMM_TILE (a tile name) and
+// FP8Q_GEMM_SPLITS, changed by gemm_force_config().
+static std::atomic<int> g_forced_tile{-2}, g_forced_splits{-1};
+
 static int env_tile() {
-    static const int v = [] {
-        const char *e = std::getenv("FP8Q_GEMM_TILE");
-        if (e)
+    int v = g_forced_tile.load(std::memory_order_relaxed);
+    if (v == -2) {
+        v = -1;
+        if (const char *e = std::getenv("FP8Q_GEMM_TILE"))
             for (int t = 0; t < T_COUNT; ++t)
-                if (std::strcmp(e, kTiles[t].name) == 0) return t;
-        return -1;
-    }();
+                if (std::strcmp(e, kTiles[t].name) == 0) v = t;
+        int expected = -2;
+        g_forced_tile.compare_exchange_strong(expected, v);
+        v = g_forced_tile.load(std::memory_order_relaxed);
+    }
     return v;
 }
 static int env_splits() {
-    static const int v = [] {
+    int v = g_forced_splits.load(std::memory_order_relaxed);
+    if (v == -1) {
         const char *e = std::getenv("FP8Q_GEMM_SPLITS");
-        const int s = e ? std::atoi(e) : 0;
-        return s >= 1 && s <= kMaxSplits ? s : 0;
-    }();
+        const int n = e ? std::atoi(e) : 0;
+        v = n >= 1 && n <= kMaxSplits ? n : 0;
+        int expected = -1;
+        g_forced_splits.compare_exchange_strong(expected, v);
+        v = g_forced_splits.load(std::memory_order_relaxed);
+    }
     return v;
 }
+
+bool gemm_force_config(int tile, int splits) {
+    if (tile < -1 || tile >= T_COUNT || splits < 0 || splits > kMaxSplits) return false;
+    g_forced_tile.store(tile, std::memory_order_relaxed);
+    g_forced_splits.store(splits, std::memory_order_relaxed);
+    return true;
+}
+
+const char *gemm_config_name(int tile) { return tile >= 0 && tile < T_COUNT ? kTiles[tile].name : nullptr; }
 
 // Split-K workspace: the arrival counters first, at a fixed place whatever the shape (a
 // later call with another shape must find zeros there), then the partial tiles.

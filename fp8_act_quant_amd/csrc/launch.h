@@ -24,5 +24,8 @@ hipError_t launch_block_gemm(const uint8_t *aq, const float *sa, const uint8_t *
                              const float *bias, void *y, bool out_bf16, bool exact, int64_t M, int64_t N,
                              int64_t K, void *workspace, size_t workspace_bytes, hipStream_t stream);
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, bool out_bf16, bool exact);
+// tuning / test hook: force a tile configuration (-1: planner) and split count (0: planner)
+bool gemm_force_config(int tile, int splits);
+const char *gemm_config_name(int tile);
 
 }  // namespace fp8q

@@ -149,6 +149,19 @@ int fp8_block_gemm_bias(const uint8_t *aq, const float *sa, const uint8_t *wq, c
  * arguments are invalid. Host-only; enqueues nothing. */
 size_t fp8_block_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int y_dtype);
 
+/* Tuning and test hook (not needed for normal use). fp8_block_gemm normally picks its tile
+ * configuration and split-K count per shape from a cost model fitted to MI355X timings.
+ * fp8q_gemm_force_config(config, splits) makes every later call in the process use tile
+ * configuration `config` (0 <= config < number of configurations; -1 restores the
+ * automatic choice) and `splits` K ranges (1..8 when the shape and workspace allow it;
+ * 0 restores the automatic choice). A configuration the contraction mode does not
+ * implement falls back to its default configuration. Returns FP8Q_ERR_SHAPE for values out
+ * of range. Process-wide and not synchronised with calls in flight on other threads.
+ * fp8q_gemm_config_name(config) names a configuration ("256x256w8": BM x BN, w8 = 8
+ * waves, s2 = two stages), or returns NULL past the last one. */
+int fp8q_gemm_force_config(int config, int splits);
+const char *fp8q_gemm_config_name(int config);
+
 /* Static string describing a status code (never NULL). */
 const char *fp8q_strerror(int status);
 

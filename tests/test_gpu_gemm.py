@@ -254,6 +254,50 @@ def test_gemm_bias_epilogue(M, N, K, out, mode):
     assert res["violations"] == 0, res
 
 
+def _configs():
+    names, i = [], 0
+    while True:
+        n = fq.lib.fp8q_gemm_config_name(i)
+        if n is None:
+            return names
+        names.append(n.decode())
+        i += 1
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 576, 2048), (129, 200, 1280)])
+def test_gemm_every_tile_configuration(M, N, K):
+    """Every tile configuration the planner can pick, forced in turn, in both contraction
+    modes and with a split-K count, on ragged shapes that span several tiles."""
+    from fp8_act_quant_amd import _lib as L
+    A = synth.random_bf16((M, K), seed=13 * M + K)
+    W = synth.random_bf16((N, K), seed=17 * N + K, std=0.02)
+    aq, sa, wq, sw = quantise_on_gpu(A, W)
+    haq, hsa, hwq, hsw = host_codes(aq), sa.cpu().numpy(), host_codes(wq), sw.cpu().numpy()
+    y_hat, bound = oracle.block_gemm(haq, hsa, hwq, hsw)
+    rows, cols = np.repeat(np.arange(M), N), np.tile(np.arange(N), M)
+    floor = scale_floor(haq, hwq, rows, cols).reshape(M, N)
+    fp8_allow = floor + mfma_group_allowance(haq, hsa, hwq, hsw, rows, cols).reshape(M, N)
+    ws = torch.zeros(64 << 20, dtype=torch.uint8, device="cuda")
+    names = _configs()
+    assert len(names) >= 8
+    try:
+        for c, name in enumerate(names):
+            for splits in (1, 2):
+                assert fq.lib.fp8q_gemm_force_config(c, splits) == L.FP8Q_OK
+                for out, mode in (("bf16", "fp8"), ("f32", "fp8"), ("f32", "exact")):
+                    if splits > 1 and mode == "exact":
+                        continue
+                    y = fq.fp8_gemm(aq, sa, wq, sw, out_dtype=TORCH_OUT[out], mode=mode, workspace=ws)
+                    torch.cuda.synchronize()
+                    res = gemm_check(y_host(y, out), y_hat, bound, out, fp8_allow if mode == "fp8" else floor)
+                    print(f"config {name} splits {splits} {out} {mode}", res, flush=True)
+                    assert res["violations"] == 0, (name, splits, out, mode, res)
+        assert fq.lib.fp8q_gemm_force_config(len(names), 0) == L.FP8Q_ERR_SHAPE
+        assert fq.lib.fp8q_gemm_force_config(0, 9) == L.FP8Q_ERR_SHAPE
+    finally:
+        fq.lib.fp8q_gemm_force_config(-1, 0)
+
+
 def test_linear_dispatch():
     """linear(): the FP8 branch is act_quant + fp8_gemm with the bias fused; the bf16
     branch dequantises the weight and applies torch's linear; a bf16 weight is used as is."""
