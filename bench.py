@@ -125,6 +125,53 @@ def cpu_baseline(A, W, rows: int):
     }, (aq, sa, y)
 
 
+def grouped_measurement(fq, L, synth, dev, stream, steps: int, warmup: int) -> dict:
+    """The routed experts' down-projection on one GPU's share of the experts: seeded top-k
+    routing (host) and N(0, 1) activations / N(0, 0.02) weights drawn on the device,
+    quantised untimed; the grouped GEMM alone is timed, one event pair per launch."""
+    import numpy as np
+    import torch
+    wl = synth.MOE_WORKLOADS["moe_down"]
+    _, offsets = synth.moe_routing(wl)
+    R, E, N, K = int(offsets[-1]), wl.local_experts, wl.N, wl.K
+    g = torch.Generator(device=dev).manual_seed(1)
+    x = torch.randn((R, K), generator=g, device=dev).to(torch.bfloat16)
+    aq, sa = fq.act_quant(x)
+    del x
+    wq = torch.empty((E, N, K), dtype=torch.float8_e4m3fn, device=dev)
+    sw = torch.empty((E, N // 128, K // 128), dtype=torch.float32, device=dev)
+    for e in range(E):
+        w = (torch.randn((N, K), generator=g, device=dev) * 0.02).to(torch.bfloat16)
+        wq[e], sw[e] = fq.weight_quant(w)
+    del w
+    off = torch.from_numpy(offsets).to(dev)
+    y = torch.empty((R, N), dtype=torch.bfloat16, device=dev)
+    args = (aq.data_ptr(), sa.data_ptr(), wq.data_ptr(), sw.data_ptr(), off.data_ptr(), y.data_ptr(),
+            L.FP8Q_OUT_BF16, E, R, N, K, stream.cuda_stream)
+    for _ in range(warmup):
+        L.check("fp8_grouped_gemm", fq.lib.fp8_grouped_gemm(*args))
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        evs[i][0].record(stream)
+        L.check("fp8_grouped_gemm", fq.lib.fp8_grouped_gemm(*args))
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    t = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e-3
+    flops = 2.0 * R * N * K
+    w_bytes = E * N * K + sw.numel() * 4
+    return {
+        "kernel": "block_gemm_kernel (grouped)",
+        "workload": f"{wl.name}: {wl.description}",
+        "rows": R, "experts": E, "N": N, "K": K, "out": "bf16",
+        "expert_rows_min_max": [int(np.diff(offsets).min()), int(np.diff(offsets).max())],
+        "avg_launch_us": round(t * 1e6, 3),
+        "tflops": round(flops / t / 1e12, 2),
+        "frac_of_fp8_peak": round(flops / t / 1e12 / FP8_PEAK_TFLOPS, 4),
+        "weight_gbs": round(w_bytes / t / 1e9, 1),
+    }
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -133,6 +180,7 @@ def main() -> int:
     ap.add_argument("--copies", type=int, default=10, help="rotated copies of A")
     ap.add_argument("--cpu-rows", type=int, default=2048, help="token rows in the CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="skip the routed-expert GEMM measurement")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the timed steps, run a plain device copy of known size (for counter scaling)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -260,6 +308,9 @@ def main() -> int:
         },
         "gemm_only_tflops": round(gemm_tflops, 2),
     }
+
+    if not args.no_extras:
+        result["grouped_gemm"] = grouped_measurement(fq, L, synth, dev, stream, args.steps, args.warmup)
 
     if not args.no_cpu_baseline:
         cb, (oaq, osa, oy) = cpu_baseline(A_host, W_host, args.cpu_rows)

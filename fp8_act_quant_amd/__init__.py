@@ -22,8 +22,8 @@ from ._lib import (FP8Q_GEMM_EXACT_SLICES, FP8Q_GEMM_FP8_PRODUCTS, FP8Q_OUT_BF16
 BLOCK = 128
 
 __all__ = [
-    "BLOCK", "Fp8qError", "act_quant", "weight_quant", "weight_dequant", "fp8_gemm", "linear",
-    "gemm_workspace_bytes", "lib",
+    "BLOCK", "Fp8qError", "act_quant", "weight_quant", "weight_dequant", "fp8_gemm", "fp8_grouped_gemm",
+    "linear", "gemm_workspace_bytes", "lib",
 ]
 
 
@@ -190,6 +190,54 @@ def fp8_gemm(a: torch.Tensor, a_s: torch.Tensor, w: torch.Tensor, w_s: torch.Ten
         check("fp8_block_gemm_bias", lib.fp8_block_gemm_bias(a.data_ptr(), a_s.data_ptr(), w.data_ptr(),
                                                              w_s.data_ptr(), b_ptr, out.data_ptr(), code, M, N, K,
                                                              ws_ptr or None, ws_bytes, _stream(a)))
+    return out
+
+
+def fp8_grouped_gemm(a: torch.Tensor, a_s: torch.Tensor, w: torch.Tensor, w_s: torch.Tensor,
+                     offsets: torch.Tensor, out_dtype=torch.bfloat16, out: torch.Tensor | None = None,
+                     mode: str = "default") -> torch.Tensor:
+    """Routed-expert block-scaled GEMM in one launch. a: float8_e4m3fn [rows, K] with scales
+    [rows, K/128], the rows of expert e being offsets[e] .. offsets[e+1]-1; w: float8_e4m3fn
+    [E, N, K] with scales [E, ceil(N/128), K/128]; offsets: int64 [E + 1] on the device,
+    non-decreasing from 0 to rows. Returns [rows, N]: row r is a[r] times the weight of the
+    expert that owns it. Rows owned by no expert (offsets not reaching rows) are left as
+    they were in `out`, or uninitialised. mode as for fp8_gemm; no split-K."""
+    if mode not in _MODES:
+        raise ValueError(f"mode must be one of {sorted(_MODES)}")
+    _need(a, "a", torch.float8_e4m3fn)
+    _need(w, "w", torch.float8_e4m3fn)
+    _need(a_s, "a_s", torch.float32, align=4)
+    _need(w_s, "w_s", torch.float32, align=4)
+    _need(offsets, "offsets", torch.int64, align=8)
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("out_dtype must be torch.float32 or torch.bfloat16")
+    if a.dim() != 2 or w.dim() != 3:
+        raise ValueError("a must be [rows, K] and w [E, N, K]")
+    rows, K = a.shape
+    E, N = w.shape[0], w.shape[1]
+    if w.shape[2] != K:
+        raise ValueError("w must be [E, N, K] with the activation's K")
+    if K % BLOCK:
+        raise ValueError("K must be a multiple of 128")
+    if tuple(a_s.shape) != (rows, K // BLOCK):
+        raise ValueError("a_s must be [rows, K/128]")
+    if tuple(w_s.shape) != (E, (N + BLOCK - 1) // BLOCK, K // BLOCK):
+        raise ValueError("w_s must be [E, ceil(N/128), K/128]")
+    if tuple(offsets.shape) != (E + 1,):
+        raise ValueError("offsets must be [E + 1]")
+    if offsets.device != a.device:
+        raise ValueError("offsets must be on the activation's device")
+    shape = (rows, N)
+    if out is None:
+        out = torch.empty(shape, dtype=out_dtype, device=a.device)
+    else:
+        _need(out, "out", out_dtype)
+        if tuple(out.shape) != shape:
+            raise ValueError(f"out must be {shape}")
+    with torch.cuda.device(a.device):
+        check("fp8_grouped_gemm", lib.fp8_grouped_gemm(a.data_ptr(), a_s.data_ptr(), w.data_ptr(), w_s.data_ptr(),
+                                                       offsets.data_ptr(), out.data_ptr(), _gemm_code(out_dtype, mode),
+                                                       E, rows, N, K, _stream(a)))
     return out
 
 

@@ -4,6 +4,7 @@
 #include <fp8q.h>
 
 #include <atomic>
+#include <cstdint>
 #include <cstring>
 
 #include "launch.h"
@@ -108,6 +109,31 @@ int fp8_block_gemm_bias(const uint8_t *aq, const float *sa, const uint8_t *wq, c
     const bool exact = mode == FP8Q_GEMM_EXACT_SLICES || (mode == 0 && dtype == FP8Q_OUT_F32);
     return finish(fp8q::launch_block_gemm(aq, sa, wq, sw, bias, y, dtype == FP8Q_OUT_BF16, exact, M, N, K,
                                           workspace, workspace_bytes, static_cast<hipStream_t>(stream)));
+}
+
+int fp8_grouped_gemm(const uint8_t *aq, const float *sa, const uint8_t *wq, const float *sw, const int64_t *offsets,
+                     void *y, int y_dtype, int64_t experts, int64_t rows, int64_t N, int64_t K, void *stream) {
+    const int dtype = y_dtype & 0xFF;
+    const int mode = y_dtype & ~0xFF;
+    if (dtype != FP8Q_OUT_F32 && dtype != FP8Q_OUT_BF16) return FP8Q_ERR_DTYPE;
+    if (mode != 0 && mode != FP8Q_GEMM_FP8_PRODUCTS && mode != FP8Q_GEMM_EXACT_SLICES) return FP8Q_ERR_DTYPE;
+    if (experts < 1 || experts > fp8q::kMaxGroupedExperts) return FP8Q_ERR_SHAPE;
+    if (int e = shape_ok(rows, K)) return e;
+    if (int e = shape_ok(N, K)) return e;
+    if (N > 0 && experts > kMaxElems / N) return FP8Q_ERR_SHAPE;
+    if (int e = shape_ok(experts * N, K)) return e;
+    if (rows > 0 && N > kMaxElems / rows) return FP8Q_ERR_SHAPE;
+    if (K > kMaxGemmK || rows > INT32_MAX / 2) return FP8Q_ERR_SHAPE;
+    if (rows == 0 || N == 0) return FP8Q_OK;
+    if (!y || !offsets) return FP8Q_ERR_NULL;
+    if (K > 0 && (!aq || !sa || !wq || !sw)) return FP8Q_ERR_NULL;
+    if (misaligned(aq, 16) || misaligned(wq, 16) || misaligned(y, 16) || misaligned(sa, 4) || misaligned(sw, 4) ||
+        misaligned(offsets, 8))
+        return FP8Q_ERR_ALIGN;
+    if (int e = check_device()) return e;
+    const bool exact = mode == FP8Q_GEMM_EXACT_SLICES || (mode == 0 && dtype == FP8Q_OUT_F32);
+    return finish(fp8q::launch_grouped_gemm(aq, sa, wq, sw, offsets, y, dtype == FP8Q_OUT_BF16, exact, experts, rows,
+                                            N, K, static_cast<hipStream_t>(stream)));
 }
 
 size_t fp8_block_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int y_dtype) {

@@ -294,11 +294,90 @@ struct GemmArgs {
     const float *bias;  // [N] fp32 added to every row before the output rounding, or null
     float *part;        // split-K partial tiles [splits][tiles][BM * BN], or null
     uint32_t *count;    // split-K arrival counter per tile, zero between calls
+    // grouped (per-expert) GEMM: expert e owns rows [offsets[e], offsets[e+1]) of A and Y and
+    // the weight wq + e*N*K (scales sw + e*ceil(N/128)*K/128); null for a plain GEMM
+    const int64_t *offsets;
     int64_t M, N, K;
     int tiles_m, tiles_n, group, splits;
+    int experts;
 };
 
-template <int BM, int BN, int NW, int WAVES_M, int NSTAGE, int OUT_BF16, int EXACT>
+constexpr int kMaxExperts = (int)kMaxGroupedExperts;
+
+// Grouped GEMM work decode, run by the whole workgroup. Expert e has c_e = ceil(rows_e / BM)
+// m-tiles; its c_e * tiles_n tiles are numbered consecutively, experts in order, and within
+// an expert the m-tile varies fastest, so the tiles that read the same weight panel are
+// adjacent. The numbers are dealt to the XCDs in contiguous runs (as in the plain GEMM) over
+// the real tile count, so surplus workgroups of the upper-bound grid are spread evenly and
+// the XCDs get equal shares. Returns false for a workgroup with no tile. Uses `scratch`
+// (LDS, at least 4 * (kMaxExperts + 1) + 16 bytes) and synchronises the workgroup. Only the
+// grouped kernel instantiations contain it, so it does not weigh on the plain GEMM's
+// registers.
+template <int BM, int NT>
+__device__ __forceinline__ bool grouped_tile(const GemmArgs &g, uint8_t *scratch, int &expert, int64_t &row0,
+                                             int64_t &row1, int &tile_n) {
+    int *prefix = reinterpret_cast<int *>(scratch);            // m-tiles before expert e
+    int *found = prefix + kMaxExperts + 1;
+    const int E = g.experts;
+    // per-expert m-tile counts; rows are clamped to [0, M] so that any offsets stay in bounds
+    constexpr int PER = (kMaxExperts + NT - 1) / NT;
+    const int e0 = threadIdx.x * PER;
+    int local[PER], sum = 0;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+        const int e = e0 + u;
+        int c = 0;
+        if (e < E) {
+            int64_t r0 = g.offsets[e], r1 = g.offsets[e + 1];
+            r0 = r0 < 0 ? 0 : (r0 > g.M ? g.M : r0);
+            r1 = r1 < r0 ? r0 : (r1 > g.M ? g.M : r1);
+            c = (int)((r1 - r0 + BM - 1) / BM);
+        }
+        local[u] = sum;
+        sum += c;
+    }
+    // exclusive scan of the per-thread sums (Hillis-Steele in LDS)
+    prefix[threadIdx.x] = sum;
+    __syncthreads();
+    for (int d = 1; d < NT; d <<= 1) {
+        const int v = threadIdx.x >= d ? prefix[threadIdx.x - d] : 0;
+        __syncthreads();
+        prefix[threadIdx.x] += v;
+        __syncthreads();
+    }
+    const int before = threadIdx.x > 0 ? prefix[threadIdx.x - 1] : 0;
+    const int total = prefix[NT - 1];
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < PER; ++u)
+        if (e0 + u <= E) prefix[e0 + u] = before + local[u];
+    if (threadIdx.x == 0) prefix[E] = total;
+    __syncthreads();
+    // XCD x (workgroups b with b % 8 == x) takes logical tiles [x*q + min(x, rem), +q + (x < rem))
+    const int units = total * g.tiles_n;
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int q = units >> 3, rem = units & 7;
+    if (slot >= q + (xcd < rem ? 1 : 0)) return false;
+    const int logical = xcd * q + (xcd < rem ? xcd : rem) + slot;
+    // the expert whose tile numbers [prefix[e] * tiles_n, prefix[e+1] * tiles_n) hold
+    // `logical` (several threads search disjoint parts; exactly one match)
+    for (int e = threadIdx.x; e < E; e += NT)
+        if (prefix[e] * g.tiles_n <= logical && logical < prefix[e + 1] * g.tiles_n) *found = e;
+    __syncthreads();
+    expert = *found;
+    const int first = prefix[expert], cnt = prefix[expert + 1] - first;
+    const int in_expert = logical - first * g.tiles_n;
+    tile_n = in_expert / cnt;
+    int64_t r0 = g.offsets[expert], r1 = g.offsets[expert + 1];
+    r0 = r0 < 0 ? 0 : (r0 > g.M ? g.M : r0);
+    r1 = r1 < r0 ? r0 : (r1 > g.M ? g.M : r1);
+    row0 = r0 + (int64_t)(in_expert - tile_n * cnt) * BM;
+    row1 = r1;
+    __syncthreads();   // the scratch is reused by the caller
+    return true;
+}
+
+template <int BM, int BN, int NW, int WAVES_M, int NSTAGE, int OUT_BF16, int EXACT, int GROUPED>
 __global__ __launch_bounds__(NW * 64) void block_gemm_kernel(GemmArgs g) {
     using S = GemmSmem<BM, BN, NSTAGE, NW>;
     constexpr int WAVES_N = NW / WAVES_M;
@@ -321,21 +400,40 @@ __global__ __launch_bounds__(NW * 64) void block_gemm_kernel(GemmArgs g) {
     // the slowest-varying part of the logical index; within one split, logical tiles run down
     // `group` tile rows before moving one tile column right, so the tiles an XCD holds at
     // once form a compact block and share A and W panels in its L2.
-    const int tiles = g.tiles_m * g.tiles_n;
-    const int units = tiles * g.splits;
-    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-    const int q = units >> 3, rem = units & 7;
-    const int logical = xcd * q + (xcd < rem ? xcd : rem) + slot;
-    const int split = logical / tiles;
-    const int tl = logical - split * tiles;
-    const int band = tl / (g.group * g.tiles_n);                 // band of `group` tile rows
-    const int in_band = tl - band * g.group * g.tiles_n;
-    const int band_rows = min(g.group, g.tiles_m - band * g.group);
-    const int tile_m = band * g.group + in_band % band_rows;
-    const int tile_n = in_band / band_rows;
-    const int64_t M = g.M, N = g.N, K = g.K;
-    const int64_t m0 = (int64_t)tile_m * BM, n0 = (int64_t)tile_n * BN;
+    const int64_t N = g.N, K = g.K;
     const int64_t nkb = K / G_SLICE;
+    const uint8_t *wq = g.wq;
+    const float *sw = g.sw;
+    int split = 0, tl = 0;
+    int64_t m0, n0, M;   // first row and column of the tile; M: end of its row range
+    if constexpr (!GROUPED) {
+        const int tiles = g.tiles_m * g.tiles_n;
+        const int units = tiles * g.splits;
+        const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+        const int q = units >> 3, rem = units & 7;
+        const int logical = xcd * q + (xcd < rem ? xcd : rem) + slot;
+        split = logical / tiles;
+        tl = logical - split * tiles;
+        const int band = tl / (g.group * g.tiles_n);             // band of `group` tile rows
+        const int in_band = tl - band * g.group * g.tiles_n;
+        const int band_rows = min(g.group, g.tiles_m - band * g.group);
+        const int tile_m = band * g.group + in_band % band_rows;
+        const int tile_n = in_band / band_rows;
+        m0 = (int64_t)tile_m * BM;
+        n0 = (int64_t)tile_n * BN;
+        M = g.M;
+    } else {
+        // grouped: the grid is an upper bound on the tiles of all experts; surplus
+        // workgroups exit
+        int expert, tile_n;
+        int64_t r0, r1;
+        if (!grouped_tile<BM, NW * 64>(g, smem, expert, r0, r1, tile_n)) return;
+        m0 = r0;
+        M = r1;
+        n0 = (int64_t)tile_n * BN;
+        wq += (int64_t)expert * N * K;
+        sw += (int64_t)expert * ((N + G_SLICE - 1) / G_SLICE) * nkb;
+    }
     const int64_t kb0 = split * nkb / g.splits, kb1 = (split + 1) * nkb / g.splits;
 
     f32x4 acc[SUB_M][SUB_N];
@@ -352,7 +450,7 @@ __global__ __launch_bounds__(NW * 64) void block_gemm_kernel(GemmArgs g) {
     for (int j = 0; j < SUB_N; ++j) sw_idx[j] = (int)(((n0 % G_SLICE) + wn * WN + 16 * j) / G_SLICE);
 
     if (kb0 < kb1) {
-        const DmaPlan<BM, BN, NSTAGE, NW, OUT_BF16 * 2 + EXACT> dma(wave, lane, g.aq, g.wq, g.sa, g.sw, m0, n0, M, N,
+        const DmaPlan<BM, BN, NSTAGE, NW, GROUPED * 4 + OUT_BF16 * 2 + EXACT> dma(wave, lane, g.aq, wq, g.sa, sw, m0, n0, M, N,
                                                                    K, nkb, smem + S::DUMMY);
         // prologue: the first NSTAGE slices in flight
 #pragma unroll
@@ -748,30 +846,22 @@ size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, bool, bool exact) {
     return split_bytes(make_plan(M, N, K, exact, 0, true));
 }
 
-template <int BM, int BN, int NW, int WAVES_M, int NSTAGE, int EXACT>
+template <int BM, int BN, int NW, int WAVES_M, int NSTAGE, int EXACT, int GROUPED = 0>
 static hipError_t launch_cfg(GemmArgs a, bool out_bf16, int splits, hipStream_t stream) {
-    a.tiles_m = (int)((a.M + BM - 1) / BM);
+    // grouped: an upper bound on the m-tiles of all experts (sum of ceil(rows_e / BM))
+    a.tiles_m = (int)((a.M + BM - 1) / BM + (a.offsets ? a.experts : 0));
     a.tiles_n = (int)((a.N + BN - 1) / BN);
     a.group = choose_group(a.tiles_m, a.tiles_n, BM, BN);
     a.splits = splits;
     const dim3 grid((unsigned)((int64_t)a.tiles_m * a.tiles_n * splits)), block(NW * 64);
     if (out_bf16)
-        block_gemm_kernel<BM, BN, NW, WAVES_M, NSTAGE, 1, EXACT><<<grid, block, 0, stream>>>(a);
+        block_gemm_kernel<BM, BN, NW, WAVES_M, NSTAGE, 1, EXACT, GROUPED><<<grid, block, 0, stream>>>(a);
     else
-        block_gemm_kernel<BM, BN, NW, WAVES_M, NSTAGE, 0, EXACT><<<grid, block, 0, stream>>>(a);
+        block_gemm_kernel<BM, BN, NW, WAVES_M, NSTAGE, 0, EXACT, GROUPED><<<grid, block, 0, stream>>>(a);
     return hipGetLastError();
 }
 
-hipError_t launch_block_gemm(const uint8_t *aq, const float *sa, const uint8_t *wq, const float *sw,
-                             const float *bias, void *y, bool out_bf16, bool exact, int64_t M, int64_t N, int64_t K,
-                             void *workspace, size_t workspace_bytes, hipStream_t stream) {
-    if (M == 0 || N == 0) return hipSuccess;
-    const GemmPlan p = make_plan(M, N, K, exact, workspace ? workspace_bytes : 0, false);
-    GemmArgs a{aq, sa, wq, sw, y, bias, nullptr, nullptr, M, N, K, 0, 0, 1, 1};
-    if (p.splits > 1) {
-        a.count = static_cast<uint32_t *>(workspace);
-        a.part = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + kCounterBytes);
-    }
+static hipError_t dispatch(const GemmPlan &p, const GemmArgs &a, bool out_bf16, bool exact, hipStream_t stream) {
     if (exact) {
         switch (p.tile) {
         case T256x128W8: return launch_cfg<256, 128, 8, 4, 3, 1>(a, out_bf16, 1, stream);
@@ -791,6 +881,31 @@ hipError_t launch_block_gemm(const uint8_t *aq, const float *sa, const uint8_t *
     case T128x128S2: return launch_cfg<128, 128, 4, 2, 2, 0>(a, out_bf16, p.splits, stream);
     default: return launch_cfg<128, 128, 4, 2, 4, 0>(a, out_bf16, p.splits, stream);
     }
+}
+
+hipError_t launch_block_gemm(const uint8_t *aq, const float *sa, const uint8_t *wq, const float *sw,
+                             const float *bias, void *y, bool out_bf16, bool exact, int64_t M, int64_t N, int64_t K,
+                             void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (M == 0 || N == 0) return hipSuccess;
+    const GemmPlan p = make_plan(M, N, K, exact, workspace ? workspace_bytes : 0, false);
+    GemmArgs a{aq, sa, wq, sw, y, bias, nullptr, nullptr, nullptr, M, N, K, 0, 0, 1, 1, 0};
+    if (p.splits > 1) {
+        a.count = static_cast<uint32_t *>(workspace);
+        a.part = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + kCounterBytes);
+    }
+    return dispatch(p, a, out_bf16, exact, stream);
+}
+
+hipError_t launch_grouped_gemm(const uint8_t *aq, const float *sa, const uint8_t *wq, const float *sw,
+                               const int64_t *offsets, void *y, bool out_bf16, bool exact, int64_t experts,
+                               int64_t rows, int64_t N, int64_t K, hipStream_t stream) {
+    if (rows == 0 || N == 0) return hipSuccess;
+    // Few tiles are instantiated for the grouped kernel: BM = 128 keeps the padding of each
+    // expert's last m-tile small; BN = 256 for wide weights, 192 otherwise.
+    GemmArgs a{aq, sa, wq, sw, y, nullptr, nullptr, nullptr, offsets, rows, N, K, 0, 0, 1, 1, (int)experts};
+    if (exact) return launch_cfg<128, 192, 8, 2, 3, 1, 1>(a, out_bf16, 1, stream);
+    if (N >= 1024) return launch_cfg<128, 256, 8, 2, 3, 0, 1>(a, out_bf16, 1, stream);
+    return launch_cfg<128, 192, 8, 2, 3, 0, 1>(a, out_bf16, 1, stream);
 }
 
 }  // namespace fp8q

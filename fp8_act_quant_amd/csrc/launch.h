@@ -24,6 +24,13 @@ hipError_t launch_block_gemm(const uint8_t *aq, const float *sa, const uint8_t *
                              const float *bias, void *y, bool out_bf16, bool exact, int64_t M, int64_t N,
                              int64_t K, void *workspace, size_t workspace_bytes, hipStream_t stream);
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, bool out_bf16, bool exact);
+
+// Grouped GEMM over `experts` weight matrices: expert e multiplies rows [offsets[e],
+// offsets[e+1]) of A (device int64 offsets, clamped to [0, rows]) by wq + e*N*K.
+constexpr int64_t kMaxGroupedExperts = 1024;
+hipError_t launch_grouped_gemm(const uint8_t *aq, const float *sa, const uint8_t *wq, const float *sw,
+                               const int64_t *offsets, void *y, bool out_bf16, bool exact, int64_t experts,
+                               int64_t rows, int64_t N, int64_t K, hipStream_t stream);
 // tuning / test hook: force a tile configuration (-1: planner) and split count (0: planner)
 bool gemm_force_config(int tile, int splits);
 const char *gemm_config_name(int tile);

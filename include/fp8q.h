@@ -144,6 +144,28 @@ int fp8_block_gemm_bias(const uint8_t *aq, const float *sa, const uint8_t *wq, c
                         const float *bias, void *y, int y_dtype, int64_t M, int64_t N, int64_t K,
                         void *workspace, size_t workspace_bytes, void *stream);
 
+/* fp8_grouped_gemm -- the block-scaled GEMMs of several experts in one launch, for the
+ * routed experts of a mixture-of-experts layer: expert e multiplies its own rows of A by its
+ * own FP8 weight. (pomoai.com "DeepSeek-V3", MoE section: each token is routed to 8 of
+ * 256 experts; FP8 section: every expert weight is stored as E4M3 128x128 blocks.)
+ *   aq [rows, K] E4M3 and sa [rows, K/128] fp32: the activation rows of all experts, those
+ *      of expert e contiguous (layout of fp8_act_quant).
+ *   wq [experts, N, K] E4M3 and sw [experts, ceil(N/128), K/128] fp32: expert e's weight
+ *      and scales (layout of fp8_weight_quant, one after another).
+ *   offsets: DEVICE int64 [experts + 1]; expert e owns rows [offsets[e], offsets[e+1]).
+ *      Expected 0 = offsets[0] <= offsets[1] <= ... <= offsets[experts] <= rows. Each
+ *      expert's range is clamped to [0, rows] (an empty range where offsets[e+1] <
+ *      offsets[e]), so nothing is read or written outside the buffers whatever the values;
+ *      ranges that overlap after clamping write their common rows more than once, in an
+ *      unspecified order. 8-byte aligned; read by the kernel, so it may be produced by
+ *      earlier work on the same stream.
+ *   y [rows, N]: row r is the output of the expert that owns it; rows owned by no expert
+ *      are not written. y_dtype as for fp8_block_gemm (output dtype and contraction mode).
+ *   1 <= experts <= 1024. No split-K, no workspace. Other conventions as fp8_block_gemm. */
+int fp8_grouped_gemm(const uint8_t *aq, const float *sa, const uint8_t *wq, const float *sw,
+                     const int64_t *offsets, void *y, int y_dtype, int64_t experts, int64_t rows,
+                     int64_t N, int64_t K, void *stream);
+
 /* Workspace size in bytes that lets fp8_block_gemm use its split-K schedule for this
  * shape and y_dtype (including the mode bits); 0 if that call does not use one or the
  * arguments are invalid. Host-only; enqueues nothing. */

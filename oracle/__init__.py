@@ -203,6 +203,41 @@ def block_gemm_sampled(aq, sa, wq, sw, rows, cols):
     return y, b
 
 
+def grouped_gemm_sampled(aq, sa, wq, sw, offsets, rows, cols):
+    """Routed-expert GEMM at outputs (rows[i], cols[i]): row r belongs to the expert e with
+    offsets[e] <= r < offsets[e+1] and is that expert's block-scaled GEMM row (the
+    composition of block_gemm_sampled over experts; wq [E, N, K], sw [E, ceil(N/128), K/128]).
+    Returns (float64 result, bound)."""
+    offsets = np.asarray(offsets, dtype=np.int64)
+    rows = np.asarray(rows, dtype=np.int64)
+    cols = np.asarray(cols, dtype=np.int64)
+    y = np.full(rows.shape, np.nan)
+    b = np.full(rows.shape, np.nan)
+    expert = np.searchsorted(offsets, rows, side="right") - 1
+    for e in np.unique(expert):
+        sel = np.nonzero(expert == e)[0]
+        r0 = offsets[e]
+        ye, be = block_gemm_sampled(aq[r0:offsets[e + 1]], sa[r0:offsets[e + 1]], wq[e], sw[e],
+                                    rows[sel] - r0, cols[sel])
+        y[sel] = ye
+        b[sel] = be
+    return y, b
+
+
+def grouped_gemm(aq, sa, wq, sw, offsets):
+    """Routed-expert GEMM, every output (rows owned by no expert are NaN)."""
+    offsets = np.asarray(offsets, dtype=np.int64)
+    R = aq.shape[0]
+    N = wq.shape[1]
+    y = np.full((R, N), np.nan)
+    b = np.full((R, N), np.nan)
+    for e in range(wq.shape[0]):
+        r0, r1 = offsets[e], offsets[e + 1]
+        if r1 > r0:
+            y[r0:r1], b[r0:r1] = block_gemm(aq[r0:r1], sa[r0:r1], wq[e], sw[e])
+    return y, b
+
+
 def matmul_bf16_sampled(x_bf16, w_bf16, rows, cols):
     """Unquantised float64 x . w^T at sampled outputs (information only)."""
     x = _c(x_bf16, np.uint16)

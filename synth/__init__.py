@@ -63,6 +63,74 @@ WORKLOADS = {
 HEADLINE = "q_down"
 
 
+@dataclass(frozen=True)
+class MoEWorkload:
+    """Routed-expert GEMM of one GPU's share of an expert-parallel MoE layer: `tokens`
+    tokens each pick `top_k` of `n_experts` experts; this GPU holds experts
+    0 .. local_experts-1, and multiplies the rows routed to each of them by that expert's
+    [N, K] weight."""
+    name: str
+    tokens: int
+    n_experts: int
+    top_k: int
+    local_experts: int
+    N: int
+    K: int
+    out_dtype: str
+    description: str = ""
+
+
+MOE_WORKLOADS = {
+    w.name: w
+    for w in [
+        MoEWorkload("moe_small", 512, 64, 6, 6, 300, 512, "bf16",
+                    "small routed-expert GEMM: 6 local experts, ragged N"),
+        MoEWorkload("moe_down", 8192, 256, 8, 32, 7168, 2048, "bf16",
+                    "routed experts' down-projection 2048 -> 7168, 32 of 256 experts (one GPU of 8), "
+                    "8192 tokens top-8"),
+    ]
+}
+
+
+def moe_routing(wl: MoEWorkload, seed: int = 0):
+    """Seeded top-k routing: per-token gate logits ~ N(0, 1) plus a per-expert bias
+    ~ N(0, 0.5^2) (experts differ in popularity), top_k experts per token. Returns (token
+    index of every row, offsets [local_experts + 1]): the rows routed to local experts,
+    grouped by expert (tokens ascending within an expert)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    bias = rng.standard_normal(wl.n_experts, dtype=np.float32) * np.float32(0.5)
+    logits = rng.standard_normal((wl.tokens, wl.n_experts), dtype=np.float32) + bias
+    top = np.argpartition(-logits, wl.top_k - 1, axis=1)[:, :wl.top_k]
+    tok = np.repeat(np.arange(wl.tokens, dtype=np.int64), wl.top_k)
+    exp = top.reshape(-1).astype(np.int64)
+    keep = exp < wl.local_experts
+    tok, exp = tok[keep], exp[keep]
+    order = np.lexsort((tok, exp))
+    tok, exp = tok[order], exp[order]
+    counts = np.bincount(exp, minlength=wl.local_experts)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    return tok, offsets
+
+
+def make_moe_inputs(wl: MoEWorkload | str, seed: int = 0):
+    """(A bf16 bits [rows, K] grouped by expert, W bf16 bits [local_experts, N, K],
+    offsets int64 [local_experts + 1]). Token activations ~ N(0, 1), weights ~ N(0, 0.02);
+    drawn after the routing from their own generator (seed + 1), activations first."""
+    if isinstance(wl, str):
+        wl = MOE_WORKLOADS[wl]
+    tok, offsets = moe_routing(wl, seed)
+    rng = np.random.Generator(np.random.PCG64(seed + 1))
+    x = rng.standard_normal((wl.tokens, wl.K), dtype=np.float32)
+    A = bf16_bits(x[tok])
+    del x
+    W = np.empty((wl.local_experts, wl.N, wl.K), dtype=np.uint16)
+    for e in range(wl.local_experts):
+        w = rng.standard_normal((wl.N, wl.K), dtype=np.float32)
+        w *= np.float32(0.02)
+        W[e] = bf16_bits(w)
+    return A, W, offsets
+
+
 def bf16_bits(a32: np.ndarray) -> np.ndarray:
     """float32 -> bf16 bit patterns (uint16), round-to-nearest-even via torch's CPU cast."""
     t = torch.from_numpy(np.ascontiguousarray(a32, dtype=np.float32))

@@ -488,3 +488,73 @@ def test_f64_to_bf16_single_rounding(oracle_lib):
     even = np.where((b & 1) == 0, b, b + 1).astype(np.uint16)
     assert np.array_equal(oracle.f64_to_bf16_array(mid), even)
     assert np.array_equal(oracle.f64_to_bf16_array(-mid), even | 0x8000)
+
+
+# ----------------------------------------------------------------------------------
+# Routed-expert GEMM (per-expert composition of the block GEMM) and its routing inputs
+# ----------------------------------------------------------------------------------
+
+def test_grouped_gemm_identifies_the_owning_expert(oracle_lib):
+    """Closed form: A's row r holds the code of 1.0 at k = r mod 128; every entry of expert
+    e's weight is the code of e + 1; unit scales. Output row r is then e + 1 for the expert
+    owning r (NaN where none does): a wrong expert or boundary shows as a wrong integer."""
+    K, N = 128, 5
+    sizes = [3, 0, 1, 4, 0, 2]
+    offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    R = int(offsets[-1]) + 2                       # two trailing rows no expert owns
+    aq = np.zeros((R, K), np.uint8)
+    aq[np.arange(R), np.arange(R) % K] = 0x38      # 1.0
+    sa = np.ones((R, 1), np.float32)
+    one_to_six = [0x38, 0x40, 0x44, 0x48, 0x4A, 0x4C]   # 1.0, 2.0, 3.0, 4.0, 5.0, 6.0
+    E = len(sizes)
+    wq = np.stack([np.full((N, K), one_to_six[e], np.uint8) for e in range(E)])
+    sw = np.ones((E, 1, 1), np.float32)
+    y, b = oracle.grouped_gemm(aq, sa, wq, sw, offsets)
+    want = np.full(R, np.nan)
+    for e in range(E):
+        want[offsets[e]:offsets[e + 1]] = e + 1
+    assert np.array_equal(y[:, 0], want, equal_nan=True)
+    assert np.all((y == want[:, None]) | np.isnan(want)[:, None])
+    # the sampled form agrees on every owned output
+    rows = np.repeat(np.arange(offsets[-1]), N)
+    cols = np.tile(np.arange(N), int(offsets[-1]))
+    ys, bs = oracle.grouped_gemm_sampled(aq, sa, wq, sw, offsets, rows, cols)
+    assert np.array_equal(ys, y[rows, cols]) and np.array_equal(bs, b[rows, cols])
+
+
+def test_grouped_gemm_invariant_under_expert_relabelling(oracle_lib):
+    """Swapping two experts together with their row blocks permutes the output rows the
+    same way."""
+    rng = np.random.Generator(np.random.PCG64(3))
+    K, N = 256, 130
+    sizes = [5, 7]
+    aq = rng.integers(0, 256, size=(12, K), dtype=np.uint8)
+    aq[(aq & 0x7F) == 0x7F] = 0
+    sa = rng.uniform(0.5, 2, size=(12, 2)).astype(np.float32)
+    wq = rng.integers(0, 256, size=(2, N, K), dtype=np.uint8)
+    wq[(wq & 0x7F) == 0x7F] = 0
+    sw = rng.uniform(0.5, 2, size=(2, 2, 2)).astype(np.float32)
+    y, _ = oracle.grouped_gemm(aq, sa, wq, sw, np.array([0, 5, 12]))
+    perm = np.r_[5:12, 0:5]
+    y2, _ = oracle.grouped_gemm(aq[perm], sa[perm], wq[::-1].copy(), sw[::-1].copy(), np.array([0, 7, 12]))
+    assert np.array_equal(y2, y[perm])
+
+
+def test_moe_routing_is_a_valid_grouping():
+    wl = synth.MOE_WORKLOADS["moe_down"]
+    tok, offsets = synth.moe_routing(wl, seed=0)
+    assert offsets[0] == 0 and offsets[-1] == len(tok) and np.all(np.diff(offsets) >= 0)
+    assert len(offsets) == wl.local_experts + 1
+    expert = np.searchsorted(offsets, np.arange(len(tok)), side="right") - 1
+    # each token once per expert, ascending within an expert, at most top_k rows per token
+    for e in range(wl.local_experts):
+        t = tok[offsets[e]:offsets[e + 1]]
+        assert np.all(np.diff(t) > 0)
+    assert np.bincount(tok, minlength=wl.tokens).max() <= wl.top_k
+    assert np.all((tok >= 0) & (tok < wl.tokens)) and np.all(expert < wl.local_experts)
+    # about tokens * top_k * local / n_experts rows; expert loads vary (biased gates)
+    mean = wl.tokens * wl.top_k * wl.local_experts / wl.n_experts
+    assert 0.5 * mean < len(tok) < 1.5 * mean
+    assert np.diff(offsets).max() > 2 * np.diff(offsets).min()
+    tok2, off2 = synth.moe_routing(wl, seed=0)
+    assert np.array_equal(tok, tok2) and np.array_equal(offsets, off2)
