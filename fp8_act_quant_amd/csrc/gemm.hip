@@ -49,6 +49,8 @@
 #include <atomic>
 #include <cstdlib>
 #include <cstring>
+#include <type_traits>
+#include <utility>
 
 #include "device_common.h"
 #include "launch.h"
@@ -65,6 +67,16 @@ typedef __attribute__((address_space(3))) void lds_void;
 constexpr int G_SLICE = 128;   // K slice = promotion interval = one f8f6f4 MFMA
 
 __device__ __forceinline__ int64_t min64(int64_t a, int64_t b) { return a < b ? a : b; }
+
+// f(std::integral_constant<int, 0>{}), ..., f(std::integral_constant<int, N - 1>{})
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 template <int BM, int BN, int NSTAGE, int NW>
 struct GemmSmem {
@@ -127,15 +139,11 @@ __device__ __forceinline__ f32x4 mfma_slice_exact(const Frag16 &a, const Frag16 
     return acc;
 }
 
-// fragment of one 16-row group: lane l supplies row (l % 16) and, with g = l / 16, the
+// Fragment of one 16-row group: lane l supplies row (l % 16) and, with g = l / 16, the
 // 16-byte chunks g and 4 + g of the 128-byte slice (k = 16g .. 16g+15 and 64+16g .. 64+16g+15).
 // Both MFMA operands use this lane -> k mapping, so matching k are paired; each 8-byte half
-// of a chunk is an aligned run of 8 consecutive k.
-__device__ __forceinline__ i32x8 load_frag(const uint8_t *base, int row, int kgroup) {
-    const u32x4 lo = *reinterpret_cast<const u32x4 *>(base + swz(row, kgroup));
-    const u32x4 hi = *reinterpret_cast<const u32x4 *>(base + swz(row, 4 + kgroup));
-    return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-}
+// of a chunk is an aligned run of 8 consecutive k. (The reads are issued in the kernel from
+// per-lane offsets computed once.)
 
 // acc += p * f per element. The empty asm consumes the result where the FMAs are written:
 // without it the compiler sinks all promotions of a slice past the branches that follow
@@ -202,7 +210,7 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *p, int64_t bytes) {
 // paddings would otherwise cost as many line requests as the tile rows themselves.)
 // VARIANT makes the type unique to each kernel instantiation: when kernels of different
 // variants shared one DmaPlan type, the host compiler emitted a launch stub for only one of them.
-template <int BM, int BN, int NSTAGE, int NW, int VARIANT>
+template <int BM, int BN, int NSTAGE, int NW, int VARIANT, int NG>
 struct DmaPlan {
     using S = GemmSmem<BM, BN, NSTAGE, NW>;
     rsrc_t ra, rw, rsa, rsw;
@@ -271,7 +279,6 @@ struct DmaPlan {
 
     // part g of NG (g a constant after unrolling) of the copies of slice kb: instructions
     // [g * PER, min((g + 1) * PER, IPW)), PER = ceil(IPW / NG)
-    template <int NG>
     __device__ __forceinline__ void issue_part(uint8_t *base, int64_t kb, int g) const {
         constexpr int PER = (S::IPW + NG - 1) / NG;
         // kb is the same in every lane; saying so keeps the offsets in SGPRs (a VGPR soffset
@@ -450,7 +457,7 @@ __global__ __launch_bounds__(NW * 64) void block_gemm_kernel(GemmArgs g) {
     for (int j = 0; j < SUB_N; ++j) sw_idx[j] = (int)(((n0 % G_SLICE) + wn * WN + 16 * j) / G_SLICE);
 
     if (kb0 < kb1) {
-        const DmaPlan<BM, BN, NSTAGE, NW, GROUPED * 4 + OUT_BF16 * 2 + EXACT> dma(wave, lane, g.aq, wq, g.sa, sw, m0, n0, M, N,
+        const DmaPlan<BM, BN, NSTAGE, NW, GROUPED * 4 + OUT_BF16 * 2 + EXACT, SUB_M> dma(wave, lane, g.aq, wq, g.sa, sw, m0, n0, M, N,
                                                                    K, nkb, smem + S::DUMMY);
         // prologue: the first NSTAGE slices in flight
 #pragma unroll
@@ -459,22 +466,46 @@ __global__ __launch_bounds__(NW * 64) void block_gemm_kernel(GemmArgs g) {
         wait_slice<S::IPW, NSTAGE - 1>((int)min64(NSTAGE, kb1 - kb0) - 1);
         lds_barrier();
 
+        // LDS byte offsets, within a stage buffer, of this lane's fragment reads and scales.
+        // The rows a wave reads are (wave base) + 16 x (group) + frow with both bases multiples
+        // of 16, so every fragment row has the swizzle of frow and its two chunk addresses are
+        // a per-lane offset plus a constant. The empty asm pins each offset in a VGPR computed
+        // once: every read is then (VGPR offset) + (compile-time stage and group offset).
+        const int frag_lo = frow * G_SLICE + (swz_chunk(frow, kgroup) << 4);
+        const int frag_hi = frow * G_SLICE + (swz_chunk(frow, 4 + kgroup) << 4);
+        int a_lo = wm * WM * G_SLICE + frag_lo, a_hi = wm * WM * G_SLICE + frag_hi;
+        int w_lo = S::A_BYTES + wn * WN * G_SLICE + frag_lo, w_hi = S::A_BYTES + wn * WN * G_SLICE + frag_hi;
+        int sa_at = S::A_BYTES + S::W_BYTES + (wm * WM + frow) * 4;
+        int sw_at[SUB_N];
+#pragma unroll
+        for (int j = 0; j < SUB_N; ++j) sw_at[j] = S::A_BYTES + S::W_BYTES + S::SA_BYTES + sw_idx[ONE_SW ? 0 : j] * 4;
+        if constexpr (NW == 8) {   // (the 4-wave tiles are short of registers: offsets recomputed there)
+            asm volatile("" : "+v"(a_lo), "+v"(a_hi), "+v"(w_lo), "+v"(w_hi), "+v"(sa_at));
+#pragma unroll
+            for (int j = 0; j < (ONE_SW ? 1 : SUB_N); ++j) asm volatile("" : "+v"(sw_at[j]));
+        }
+        auto frag_at = [&](const uint8_t *base, int lo, int hi) __device__ __attribute__((always_inline)) {
+            const u32x4 l = *reinterpret_cast<const u32x4 *>(base + lo);
+            const u32x4 h = *reinterpret_cast<const u32x4 *>(base + hi);
+            return i32x8{(int)l.x, (int)l.y, (int)l.z, (int)l.w, (int)h.x, (int)h.y, (int)h.z, (int)h.w};
+        };
+        auto f32_at = [&](const uint8_t *base, int off) __device__ __attribute__((always_inline)) {
+            return *reinterpret_cast<const float *>(base + off);
+        };
+
         // fragments of the slice being contracted
         i32x8 wf[SUB_N];
         Frag16 wh[EXACT ? SUB_N : 1];
         float swv[SUB_N];
         i32x8 af;
         float sav;
-        auto load_slice_head = [&](const uint8_t *stage) {
-            const uint8_t *tW = stage + S::A_BYTES;
-            const float *tS = reinterpret_cast<const float *>(stage + S::A_BYTES + S::W_BYTES);
-            const float *tSW = reinterpret_cast<const float *>(stage + S::A_BYTES + S::W_BYTES + S::SA_BYTES);
+        auto load_slice_head = [&](const uint8_t *stage) __device__ __attribute__((always_inline)) {
 #pragma unroll
-            for (int j = 0; j < SUB_N; ++j) wf[j] = load_frag(tW, wn * WN + 16 * j + frow, kgroup);
-            af = load_frag(stage, wm * WM + frow, kgroup);
-            sav = tS[wm * WM + frow];
+            for (int j = 0; j < SUB_N; ++j) wf[j] = frag_at(stage + 16 * j * G_SLICE, w_lo, w_hi);
+            af = frag_at(stage, a_lo, a_hi);
+            sav = f32_at(stage, sa_at);
 #pragma unroll
-            for (int j = 0; j < SUB_N; ++j) swv[j] = ONE_SW ? tSW[sw_idx[0]] : tSW[sw_idx[j]];
+            for (int j = 0; j < SUB_N; ++j) swv[j] = f32_at(stage, sw_at[ONE_SW ? 0 : j]);
             if constexpr (EXACT) {
 #pragma unroll
                 for (int j = 0; j < SUB_N; ++j) wh[j] = to_f16(wf[j]);
@@ -497,31 +528,41 @@ __global__ __launch_bounds__(NW * 64) void block_gemm_kernel(GemmArgs g) {
             p_prev[j] = f32x4{0.f, 0.f, 0.f, 0.f};
             f_prev[j] = 0.f;
         }
-        int st = 0;
-        for (int64_t kb = kb0; kb < kb1; ++kb) {
-            const uint8_t *stage = smem + st * S::STAGE;
-            const float *tS = reinterpret_cast<const float *>(stage + S::A_BYTES + S::W_BYTES);
-            const int st_next = st + 1 == NSTAGE ? 0 : st + 1;
-            const bool more = kb + 1 < kb1;
+        // With 8 waves the K loop is unrolled by NSTAGE: each slice's stage buffer, the buffer
+        // its copies go to and the next slice's buffer are then compile-time offsets, so
+        // fragment reads use fixed addresses and the loop carries no stage index. (The 4-wave
+        // tiles hold twice the accumulators per wave; unrolled, they run out of registers, so
+        // they keep a rolled loop with a stage index.) The slice indices are wave-uniform
+        // 32-bit values, which keeps the copy and barrier conditions scalar.
+        const int kbs = __builtin_amdgcn_readfirstlane((int)kb0);
+        const int kbe = __builtin_amdgcn_readfirstlane((int)kb1);
+        // slice kb in `stage`, whose copies (slice kb + NSTAGE - 1) go to `copy_dst`, followed
+        // by the slice in `next`. A steady slice (not the first, and at least NSTAGE - 1 slices
+        // before the end) always queues copies and always has a successor: its body has no
+        // branches.
+        auto slice = [&](const uint8_t *stage, uint8_t *copy_dst, const uint8_t *next, const int kb, auto steady_c)
+                         __device__ __attribute__((always_inline)) {
+            constexpr bool STEADY = decltype(steady_c)::value;
+            const bool more = STEADY || kb + 1 < kbe;
+            const int later = STEADY ? NSTAGE - 2 : min(NSTAGE - 2, kbe - 2 - kb);
             // the copies of slice kb + NSTAGE - 1 go into the buffer of slice kb - 1, free since
             // the barrier that ended slice kb - 1; they are spread over this slice's row groups
             // so that the matrix unit is never left waiting behind a burst of copy issues
-            const bool copy_now = kb > kb0 && kb + NSTAGE - 1 < kb1;
-            uint8_t *const copy_dst = smem + (st == 0 ? NSTAGE - 1 : st - 1) * S::STAGE;
+            const bool copy_now = STEADY || (kb > kbs && kb + NSTAGE - 1 < kbe);
 #pragma unroll
             for (int i = 0; i < SUB_M; ++i) {
                 if (EARLY_BARRIER && i == SUB_M - 1 && more) {
                     // every LDS read of slice kb is done (the last group's operands are in
                     // registers); once all waves are past the barrier the next slice has landed
                     wait_lgkm0();
-                    wait_slice<S::IPW, NSTAGE - 2>((int)min64(NSTAGE - 2, kb1 - 1 - (kb + 1)));
+                    wait_slice<S::IPW, NSTAGE - 2>(later);
                     lds_barrier();
                 }
                 i32x8 af_n = af;
                 float sav_n = sav;
                 if (i + 1 < SUB_M) {
-                    af_n = load_frag(stage, wm * WM + 16 * (i + 1) + frow, kgroup);
-                    sav_n = tS[wm * WM + 16 * (i + 1) + frow];
+                    af_n = frag_at(stage + 16 * (i + 1) * G_SLICE, a_lo, a_hi);
+                    sav_n = f32_at(stage + 16 * (i + 1) * 4, sa_at);
                 }
                 float f_cur[SUB_N];
 #pragma unroll
@@ -533,7 +574,7 @@ __global__ __launch_bounds__(NW * 64) void block_gemm_kernel(GemmArgs g) {
 #pragma unroll
                     for (int j = 0; j < SUB_N; ++j) {
                         p_cur[j] = mfma_slice_exact(wh[j], ah);
-                        if (j == 0 && copy_now) dma.template issue_part<SUB_M>(copy_dst, kb + NSTAGE - 1, i);
+                        if (j == 0 && copy_now) dma.issue_part(copy_dst, kb + NSTAGE - 1, i);
                         promote(acc[ip][j], p_prev[j], f_prev[j]);
                         __builtin_amdgcn_sched_barrier(0);
                     }
@@ -541,7 +582,7 @@ __global__ __launch_bounds__(NW * 64) void block_gemm_kernel(GemmArgs g) {
 #pragma unroll
                     for (int j = 0; j < SUB_N; ++j) {
                         p_cur[j] = mfma_slice(wf[j], af);
-                        if (j == 0 && copy_now) dma.template issue_part<SUB_M>(copy_dst, kb + NSTAGE - 1, i);
+                        if (j == 0 && copy_now) dma.issue_part(copy_dst, kb + NSTAGE - 1, i);
                         promote(acc[ip][j], p_prev[j], f_prev[j]);
                         __builtin_amdgcn_sched_barrier(0);
                     }
@@ -550,10 +591,10 @@ __global__ __launch_bounds__(NW * 64) void block_gemm_kernel(GemmArgs g) {
                 // fragments load while they run
                 if (i == SUB_M - 1 && more) {
                     if (!EARLY_BARRIER) {
-                        wait_slice<S::IPW, NSTAGE - 2>((int)min64(NSTAGE - 2, kb1 - 1 - (kb + 1)));
+                        wait_slice<S::IPW, NSTAGE - 2>(later);
                         lds_barrier();
                     }
-                    load_slice_head(smem + st_next * S::STAGE);
+                    load_slice_head(next);
                 }
 #pragma unroll
                 for (int j = 0; j < SUB_N; ++j) {
@@ -565,7 +606,34 @@ __global__ __launch_bounds__(NW * 64) void block_gemm_kernel(GemmArgs g) {
                     sav = sav_n;
                 }
             }
-            st = st_next;
+        };
+        const std::false_type general;
+        const std::true_type steady;
+        if constexpr (NW == 8) {
+            // slice kb uses stage (kb - kbs) % NSTAGE, a constant in each unrolled copy
+            auto at = [&](int st) __device__ __attribute__((always_inline)) { return smem + (st % NSTAGE) * S::STAGE; };
+            slice(at(0), at(NSTAGE - 1), at(1), kbs, general);
+            int kb = kbs + 1;
+            // whole rounds of steady slices (stages 1, 2, ..., 0)
+            for (; kb + 2 * NSTAGE - 2 < kbe; kb += NSTAGE)
+                static_for<NSTAGE>([&](auto t) __device__ __attribute__((always_inline)) {
+                    constexpr int st = 1 + decltype(t)::value;
+                    slice(at(st), at(st + NSTAGE - 1), at(st + 1), kb + decltype(t)::value, steady);
+                });
+            // the last (at most 2 NSTAGE - 2) slices
+            static_for<2 * NSTAGE - 2>([&](auto t) __device__ __attribute__((always_inline)) {
+                constexpr int st = 1 + decltype(t)::value;
+                if (kb + decltype(t)::value < kbe)
+                    slice(at(st), at(st + NSTAGE - 1), at(st + 1), kb + decltype(t)::value, general);
+            });
+        } else {
+            int st = 0;
+            for (int kb = kbs; kb < kbe; ++kb) {
+                const int st_next = st + 1 == NSTAGE ? 0 : st + 1;
+                const int st_copy = st == 0 ? NSTAGE - 1 : st - 1;
+                slice(smem + st * S::STAGE, smem + st_copy * S::STAGE, smem + st_next * S::STAGE, kb, general);
+                st = st_next;
+            }
         }
 #pragma unroll
         for (int j = 0; j < SUB_N; ++j) promote(acc[SUB_M - 1][j], p_prev[j], f_prev[j]);
@@ -704,7 +772,7 @@ __global__ __launch_bounds__(NW * 64) void block_gemm_kernel(GemmArgs g) {
 // one K slice of one tile, and the fixed cost of a tile (first copies in flight, output
 // stores).
 enum GemmTile {
-    T256x256W8 = 0, T256x192W8, T256x128W8, T128x256W8, T128x192W8, T128x192, T256x128, T128x128, T128x128S2,
+    T256x256W8 = 0, T256x192W8, T256x128W8, T128x256W8, T128x192W8, T256x128, T128x128, T128x128S2,
     T_COUNT
 };
 
@@ -718,8 +786,7 @@ struct TileInfo {
 static const TileInfo kTiles[T_COUNT] = {
     {"256x256w8", 256, 256, true, false, 2.09, 14.5}, {"256x192w8", 256, 192, true, false, 2.04, 10.0},
     {"256x128w8", 256, 128, true, true, 1.62, 5.8},   {"128x256w8", 128, 256, true, true, 1.58, 6.0},
-    {"128x192w8", 128, 192, true, true, 1.08, 4.4},   {"128x192", 128, 192, true, false, 1.21, 4.4},
-    {"256x128", 256, 128, true, false, 1.44, 5.8},
+    {"128x192w8", 128, 192, true, true, 1.08, 4.4},   {"256x128", 256, 128, true, false, 1.44, 5.8},
     {"128x128", 128, 128, true, true, 1.05, 3.0},     {"128x128s2", 128, 128, false, false, 1.05, 3.0},
 };
 
@@ -876,7 +943,6 @@ static hipError_t dispatch(const GemmPlan &p, const GemmArgs &a, bool out_bf16, 
     case T256x128W8: return launch_cfg<256, 128, 8, 4, 3, 0>(a, out_bf16, p.splits, stream);
     case T128x256W8: return launch_cfg<128, 256, 8, 2, 3, 0>(a, out_bf16, p.splits, stream);
     case T128x192W8: return launch_cfg<128, 192, 8, 2, 3, 0>(a, out_bf16, p.splits, stream);
-    case T128x192: return launch_cfg<128, 192, 4, 2, 3, 0>(a, out_bf16, p.splits, stream);
     case T256x128: return launch_cfg<256, 128, 4, 2, 3, 0>(a, out_bf16, p.splits, stream);
     case T128x128S2: return launch_cfg<128, 128, 4, 2, 2, 0>(a, out_bf16, p.splits, stream);
     default: return launch_cfg<128, 128, 4, 2, 4, 0>(a, out_bf16, p.splits, stream);
