@@ -65,7 +65,9 @@ def _per_dispatch(csv_path: str, counter: str):
             if row.get("Counter_Name") != counter:
                 continue
             name = row["Kernel_Name"]
-            key = ("gemm" if "block_gemm_kernel" in name else "act_quant" if "act_quant_kernel" in name
+            # the plain GEMM (the grouped instantiation has GROUPED = 1 as its last template argument)
+            plain_gemm = "block_gemm_kernel" in name and name.split(">")[0].split(",")[-1].strip() == "0"
+            key = ("gemm" if plain_gemm else "act_quant" if "act_quant_kernel" in name
                    else "copy" if "MulFunctor" in name else None)
             if key is None:
                 continue
@@ -182,7 +184,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the routed-expert GEMM measurement")
     ap.add_argument("--calibrate-copy", action="store_true",
-                    help="after the timed steps, run a plain device copy of known size (for counter scaling)")
+                    help="after the timed steps, run a plain device copy of known size (for counter scaling); "
+                         "skips the routed-expert measurement")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the GEMM's HBM traffic summary from two rocprofv3 --pmc runs and exit")
     args = ap.parse_args()
@@ -309,7 +312,7 @@ def main() -> int:
         "gemm_only_tflops": round(gemm_tflops, 2),
     }
 
-    if not args.no_extras:
+    if not args.no_extras and not args.calibrate_copy:   # (counter runs: the calibration kernel must be the only multiply)
         result["grouped_gemm"] = grouped_measurement(fq, L, synth, dev, stream, args.steps, args.warmup)
 
     if not args.no_cpu_baseline:

@@ -768,9 +768,9 @@ __global__ __launch_bounds__(NW * 64) void block_gemm_kernel(GemmArgs g) {
 // host side: tile and split choice, workspace, launch
 
 // Tile configurations: (BM, BN, waves, waves along M, stages). The timing columns are
-// measured on MI355X (FP8 products, full-size workloads, every CU busy): the duration of
-// one K slice of one tile, and the fixed cost of a tile (first copies in flight, output
-// stores).
+// measured on MI355X (bf16 output, 512 tiles on 256 CUs, K = 1024 and 4096), per
+// contraction mode: the duration of one K slice of one tile, and the fixed cost of a tile
+// (first copies in flight, output stores).
 enum GemmTile {
     T256x256W8 = 0, T256x192W8, T256x128W8, T128x256W8, T128x192W8, T256x128, T128x128, T128x128S2,
     T_COUNT
@@ -780,14 +780,15 @@ struct TileInfo {
     const char *name;
     int bm, bn;
     bool fp8_ok, exact_ok;
-    double us_slice, us_fixed;
+    double us_slice, us_fixed;       // FP8-product mode
+    double us_slice_x, us_fixed_x;   // exact-slice mode (0: not implemented)
 };
 
 static const TileInfo kTiles[T_COUNT] = {
-    {"256x256w8", 256, 256, true, false, 2.09, 14.5}, {"256x192w8", 256, 192, true, false, 2.04, 10.0},
-    {"256x128w8", 256, 128, true, true, 1.62, 5.8},   {"128x256w8", 128, 256, true, true, 1.58, 6.0},
-    {"128x192w8", 128, 192, true, true, 1.08, 4.4},   {"256x128", 256, 128, true, false, 1.44, 5.8},
-    {"128x128", 128, 128, true, true, 1.05, 3.0},     {"128x128s2", 128, 128, false, false, 1.05, 3.0},
+    {"256x256w8", 256, 256, true, false, 1.84, 10.0, 0, 0},      {"256x192w8", 256, 192, true, false, 1.59, 7.5, 0, 0},
+    {"256x128w8", 256, 128, true, true, 1.02, 7.0, 2.04, 5.9},   {"128x256w8", 128, 256, true, true, 0.94, 7.0, 2.10, 4.7},
+    {"128x192w8", 128, 192, true, true, 0.78, 5.9, 1.61, 4.7},   {"256x128", 256, 128, true, false, 1.22, 7.1, 0, 0},
+    {"128x128", 128, 128, true, true, 0.82, 4.4, 1.36, 4.6},     {"128x128s2", 128, 128, false, false, 0.95, 2.8, 0, 0},
 };
 
 constexpr int kNumCUs = 256;
@@ -874,12 +875,14 @@ static size_t split_bytes(const GemmPlan &p) {
 // Estimated duration (us): full waves of workgroups times the slices each contracts plus
 // its fixed cost, plus the split-K reduction (the last workgroup of a tile reads the other
 // splits' partials; all of them write theirs).
-static double plan_cost(int tile, int64_t tiles, int splits, int64_t nkb) {
+static double plan_cost(int tile, int64_t tiles, int splits, int64_t nkb, bool exact) {
     const TileInfo &t = kTiles[tile];
+    const double us_slice = exact && t.us_slice_x > 0 ? t.us_slice_x : t.us_slice;
+    const double us_fixed = exact && t.us_slice_x > 0 ? t.us_fixed_x : t.us_fixed;
     const double kouts = t.bm * t.bn / 1024.0;
     const int64_t units = tiles * splits;
     const int64_t waves = (units + kNumCUs - 1) / kNumCUs;
-    const double per_unit = (double)((nkb + splits - 1) / splits) * t.us_slice + t.us_fixed;
+    const double per_unit = (double)((nkb + splits - 1) / splits) * us_slice + us_fixed;
     return waves * per_unit + (splits - 1) * 0.23 * kouts;
 }
 
@@ -898,7 +901,7 @@ static GemmPlan make_plan(int64_t M, int64_t N, int64_t K, bool exact, size_t ws
             const GemmPlan p{t, s, tm, tn};
             if (s > 1 && !size_query && split_bytes(p) > ws_bytes) break;
             if (forced_splits && s != forced_splits && s != 1) continue;
-            double c = plan_cost(t, tm * tn, s, nkb);
+            double c = plan_cost(t, tm * tn, s, nkb, exact);
             if (forced_splits && s == 1 && forced_splits != 1) c += 1e200;   // only if the forced count is impossible
             if (c < best_cost) {
                 best_cost = c;
