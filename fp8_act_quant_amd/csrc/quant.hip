@@ -61,7 +61,11 @@ __global__ __launch_bounds__(AQ_THREADS) void act_quant_kernel(const u32x4 *__re
             const TileScale ts = tile_scale(amax);
             const u32x2 codes = quant8(v[u], ts);
             if (t < n_tiles) {
-                __builtin_nontemporal_store(codes, &q[t * 16 + j]);
+                // an ordinary (cache-allocating) store: the codes (1 B per element) are read
+                // by the GEMM right after, and staying in the 256 MB MALL saves it the HBM
+                // round trip (measured: GEMM -8%, act_quant +5%, step -2.4%); the bf16 input
+                // is streamed with non-temporal loads
+                q[t * 16 + j] = codes;
                 if (j == 0) s[t] = ts.s;
             }
         }
