@@ -457,7 +457,19 @@ __global__ __launch_bounds__(NW * 64) void block_gemm_kernel(GemmArgs g) {
     for (int j = 0; j < SUB_N; ++j) sw_idx[j] = (int)(((n0 % G_SLICE) + wn * WN + 16 * j) / G_SLICE);
 
     if (kb0 < kb1) {
-        const DmaPlan<BM, BN, NSTAGE, NW, GROUPED * 4 + OUT_BF16 * 2 + EXACT, SUB_M> dma(wave, lane, g.aq, wq, g.sa, sw, m0, n0, M, N,
+        // Where the slice barrier sits. With three or more stages the copies have slack, and
+        // the barrier goes before the last row group: that group's MFMAs (operands already in
+        // registers) then run while the next slice's first fragments are read. With two
+        // stages the next slice's copies have only one slice of lead, and the barrier goes
+        // after the last group's MFMAs, as late as possible (measured: 4% faster there).
+        constexpr bool EARLY_BARRIER = NSTAGE >= 3;
+        // The copies queued during a slice are spread over the row groups that run before its
+        // barrier (all of them with the late barrier), so that at the barrier every slice
+        // queued after the next one is complete in the vector-memory count and the count
+        // wait of wait_slice covers exactly the next slice.
+        constexpr int COPY_PARTS = EARLY_BARRIER ? SUB_M - 1 : SUB_M;
+        static_assert(COPY_PARTS >= 1, "row groups per wave");
+        const DmaPlan<BM, BN, NSTAGE, NW, GROUPED * 4 + OUT_BF16 * 2 + EXACT, COPY_PARTS> dma(wave, lane, g.aq, wq, g.sa, sw, m0, n0, M, N,
                                                                    K, nkb, smem + S::DUMMY);
         // prologue: the first NSTAGE slices in flight
 #pragma unroll
@@ -513,12 +525,6 @@ __global__ __launch_bounds__(NW * 64) void block_gemm_kernel(GemmArgs g) {
         };
         load_slice_head(smem);
 
-        // Where the slice barrier sits. With three or more stages the copies have slack, and
-        // the barrier goes before the last row group: that group's MFMAs (operands already in
-        // registers) then run while the next slice's first fragments are read. With two
-        // stages the next slice's copies have only one slice of lead, and the barrier goes
-        // after the last group's MFMAs, as late as possible (measured: 4% faster there).
-        constexpr bool EARLY_BARRIER = NSTAGE >= 3;
         // promotion of each row group runs one group behind its MFMAs (the last group of a
         // slice is promoted during the first group of the next); it starts from a zero partial
         f32x4 p_prev[SUB_N];
@@ -551,22 +557,31 @@ __global__ __launch_bounds__(NW * 64) void block_gemm_kernel(GemmArgs g) {
             const bool copy_now = STEADY || (kb > kbs && kb + NSTAGE - 1 < kbe);
 #pragma unroll
             for (int i = 0; i < SUB_M; ++i) {
-                if (EARLY_BARRIER && i == SUB_M - 1 && more) {
+                // With the early barrier, the next slice's first fragments and scales are read
+                // right after it, while this slice's last row group runs on the matrix unit:
+                // each W fragment register is refilled as soon as its last MFMA has taken it.
+                const bool head_now = EARLY_BARRIER && i == SUB_M - 1 && more;
+                i32x8 af_n = af;
+                float sav_n = sav;
+                if (head_now) {
                     // every LDS read of slice kb is done (the last group's operands are in
                     // registers); once all waves are past the barrier the next slice has landed
                     wait_lgkm0();
                     wait_slice<S::IPW, NSTAGE - 2>(later);
                     lds_barrier();
-                }
-                i32x8 af_n = af;
-                float sav_n = sav;
-                if (i + 1 < SUB_M) {
+                    af_n = frag_at(next, a_lo, a_hi);
+                    sav_n = f32_at(next, sa_at);
+                } else if (i + 1 < SUB_M) {
                     af_n = frag_at(stage + 16 * (i + 1) * G_SLICE, a_lo, a_hi);
                     sav_n = f32_at(stage + 16 * (i + 1) * 4, sa_at);
                 }
                 float f_cur[SUB_N];
 #pragma unroll
                 for (int j = 0; j < SUB_N; ++j) f_cur[j] = sav * (ONE_SW ? swv[0] : swv[j]);
+                if (head_now) {
+#pragma unroll
+                    for (int j = 0; j < SUB_N; ++j) swv[j] = f32_at(next, sw_at[ONE_SW ? 0 : j]);
+                }
                 f32x4 p_cur[SUB_N];
                 const int ip = i == 0 ? SUB_M - 1 : i - 1;   // row group being promoted (a constant once unrolled)
                 if constexpr (EXACT) {
@@ -574,26 +589,30 @@ __global__ __launch_bounds__(NW * 64) void block_gemm_kernel(GemmArgs g) {
 #pragma unroll
                     for (int j = 0; j < SUB_N; ++j) {
                         p_cur[j] = mfma_slice_exact(wh[j], ah);
-                        if (j == 0 && copy_now) dma.issue_part(copy_dst, kb + NSTAGE - 1, i);
+                        if (j == 0 && copy_now && i < COPY_PARTS) dma.issue_part(copy_dst, kb + NSTAGE - 1, i);
+                        if (head_now) wf[j] = frag_at(next + 16 * j * G_SLICE, w_lo, w_hi);
                         promote(acc[ip][j], p_prev[j], f_prev[j]);
                         __builtin_amdgcn_sched_barrier(0);
+                    }
+                    if (head_now) {
+#pragma unroll
+                        for (int j = 0; j < SUB_N; ++j) wh[j] = to_f16(wf[j]);
                     }
                 } else {
 #pragma unroll
                     for (int j = 0; j < SUB_N; ++j) {
                         p_cur[j] = mfma_slice(wf[j], af);
-                        if (j == 0 && copy_now) dma.issue_part(copy_dst, kb + NSTAGE - 1, i);
+                        if (j == 0 && copy_now && i < COPY_PARTS) dma.issue_part(copy_dst, kb + NSTAGE - 1, i);
+                        if (head_now) wf[j] = frag_at(next + 16 * j * G_SLICE, w_lo, w_hi);
                         promote(acc[ip][j], p_prev[j], f_prev[j]);
                         __builtin_amdgcn_sched_barrier(0);
                     }
                 }
-                // the last group's MFMAs have taken their operands: the next slice's first
-                // fragments load while they run
-                if (i == SUB_M - 1 && more) {
-                    if (!EARLY_BARRIER) {
-                        wait_slice<S::IPW, NSTAGE - 2>(later);
-                        lds_barrier();
-                    }
+                // with the late barrier (two stages) the next slice's first fragments load after
+                // the last group's MFMAs have taken their operands, while they run
+                if (!EARLY_BARRIER && i == SUB_M - 1 && more) {
+                    wait_slice<S::IPW, NSTAGE - 2>(later);
+                    lds_barrier();
                     load_slice_head(next);
                 }
 #pragma unroll
@@ -601,7 +620,7 @@ __global__ __launch_bounds__(NW * 64) void block_gemm_kernel(GemmArgs g) {
                     p_prev[j] = p_cur[j];
                     f_prev[j] = f_cur[j];
                 }
-                if (i + 1 < SUB_M) {
+                if (i + 1 < SUB_M || head_now) {
                     af = af_n;
                     sav = sav_n;
                 }
