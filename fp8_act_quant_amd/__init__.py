@@ -23,7 +23,8 @@ BLOCK = 128
 
 __all__ = [
     "BLOCK", "Fp8qError", "act_quant", "weight_quant", "weight_dequant", "fp8_gemm", "fp8_grouped_gemm",
-    "linear", "gemm_workspace_bytes", "lib",
+    "linear", "gemm_workspace_bytes", "lib", "act_quant_t", "weight_transpose", "fp8_gemm_rowwise",
+    "linear_backward",
 ]
 
 
@@ -262,3 +263,102 @@ def linear(x: torch.Tensor, weight: torch.Tensor, bias: torch.Tensor | None = No
         raise ValueError('gemm_impl must be "fp8" or "bf16"')
     q, s = act_quant(x)
     return fp8_gemm(q, s, weight, weight_scale, out_dtype=out_dtype, bias=bias)
+
+
+# ---------------------------------------------------------------------------------------
+# Training GEMMs (backward of y = x W^T): see include/fp8q.h for the quantisation reading.
+
+def act_quant_t(x: torch.Tensor):
+    """Token-wise quantisation of a bf16 [M, C] tensor (C a multiple of 8), transposed:
+    returns ``(qt, st)``, qt float8_e4m3fn [C, ldq] and st float32 [C, ldq/128] with
+    ldq = ceil(M/128)*128; tokens past M are code 0."""
+    _need(x, "x", torch.bfloat16)
+    if x.dim() != 2:
+        raise ValueError("x must be [M, C]")
+    M, C = x.shape
+    if C % 8:
+        raise ValueError("C must be a multiple of 8")
+    ldq = -(-M // BLOCK) * BLOCK
+    qt = torch.empty((C, ldq), dtype=torch.float8_e4m3fn, device=x.device)
+    st = torch.empty((C, ldq // BLOCK), dtype=torch.float32, device=x.device)
+    with torch.cuda.device(x.device):
+        check("fp8_act_quant_t", lib.fp8_act_quant_t(x.data_ptr(), qt.data_ptr(), st.data_ptr(), M, C, _stream(x)))
+    return qt, st
+
+
+def weight_transpose(q: torch.Tensor, s: torch.Tensor):
+    """FP8 weight [N, K] and its block scales [ceil(N/128), K/128] -> the transposed weight
+    [K, N] and scales [K/128, ceil(N/128)] (the same codes and block scales)."""
+    _need(q, "q", torch.float8_e4m3fn)
+    _need(s, "s", torch.float32, align=4)
+    N, K = q.shape
+    if K % BLOCK or tuple(s.shape) != ((N + BLOCK - 1) // BLOCK, K // BLOCK):
+        raise ValueError("q must be [N, K] (K a multiple of 128) with scales [ceil(N/128), K/128]")
+    qt = torch.empty((K, N), dtype=torch.float8_e4m3fn, device=q.device)
+    st = torch.empty((K // BLOCK, (N + BLOCK - 1) // BLOCK), dtype=torch.float32, device=q.device)
+    with torch.cuda.device(q.device):
+        check("fp8_weight_transpose", lib.fp8_weight_transpose(q.data_ptr(), s.data_ptr(), qt.data_ptr(),
+                                                               st.data_ptr(), N, K, _stream(q)))
+    return qt, st
+
+
+def fp8_gemm_rowwise(a: torch.Tensor, a_s: torch.Tensor, b: torch.Tensor, b_s: torch.Tensor,
+                     out_dtype=torch.float32, workspace="auto", out: torch.Tensor | None = None,
+                     mode: str = "default") -> torch.Tensor:
+    """Y [M, N] = A . B^T with per-row scales on both operands: a float8_e4m3fn [M, K] with
+    scales [M, K/128], b float8_e4m3fn [N, K] with scales [N, K/128]. mode and workspace as
+    for fp8_gemm."""
+    if mode not in _MODES:
+        raise ValueError(f"mode must be one of {sorted(_MODES)}")
+    for t, n, dt, al in ((a, "a", torch.float8_e4m3fn, 16), (b, "b", torch.float8_e4m3fn, 16),
+                         (a_s, "a_s", torch.float32, 4), (b_s, "b_s", torch.float32, 4)):
+        _need(t, n, dt, align=al)
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("out_dtype must be torch.float32 or torch.bfloat16")
+    if a.dim() != 2 or b.dim() != 2 or a.shape[1] != b.shape[1] or a.shape[1] % BLOCK:
+        raise ValueError("a [M, K] and b [N, K] with K a multiple of 128")
+    M, K = a.shape
+    N = b.shape[0]
+    if tuple(a_s.shape) != (M, K // BLOCK) or tuple(b_s.shape) != (N, K // BLOCK):
+        raise ValueError("a_s must be [M, K/128] and b_s [N, K/128]")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=a.device)
+    else:
+        _need(out, "out", out_dtype)
+        if tuple(out.shape) != (M, N):
+            raise ValueError(f"out must be {(M, N)}")
+    code = _gemm_code(out_dtype, mode)
+    ws_ptr, ws_bytes = 0, 0
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError('workspace must be "auto", None or a tensor')
+        need = int(lib.fp8_rowwise_gemm_workspace_bytes(M, N, K, code)) if M and N and K else 0
+        if need:
+            ws = _auto_workspace(a.device, _stream(a), need)
+            ws_ptr, ws_bytes = ws.data_ptr(), ws.numel()
+    elif workspace is not None:
+        _need(workspace, "workspace", workspace.dtype)
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    with torch.cuda.device(a.device):
+        check("fp8_rowwise_gemm", lib.fp8_rowwise_gemm(a.data_ptr(), a_s.data_ptr(), b.data_ptr(), b_s.data_ptr(),
+                                                       out.data_ptr(), code, M, N, K, ws_ptr or None, ws_bytes,
+                                                       _stream(a)))
+    return out
+
+
+def linear_backward(dy: torch.Tensor, x: torch.Tensor, weight: torch.Tensor, weight_scale: torch.Tensor,
+                    weight_t=None, dx_dtype=torch.bfloat16, dw_dtype=torch.float32):
+    """FP8 backward of y = x W^T (W an FP8 weight [N, K] with 128x128 block scales):
+    dx [M, K] = dY . W (dY quantised 1x128 along N; N a multiple of 128) and
+    dW [N, K] = dY^T . X (both quantised 1x128 along the tokens). weight_t: optional
+    (W^T codes, scales) from weight_transpose, reused across steps. Returns (dx, dw)."""
+    if dy.dim() != 2 or x.dim() != 2 or dy.shape[0] != x.shape[0]:
+        raise ValueError("dy [M, N] and x [M, K]")
+    if weight_t is None:
+        weight_t = weight_transpose(weight, weight_scale)
+    dyq, sdy = act_quant(dy)
+    dx = fp8_gemm(dyq, sdy, weight_t[0], weight_t[1], out_dtype=dx_dtype)
+    dyt, sdyt = act_quant_t(dy)
+    xt, sxt = act_quant_t(x)
+    dw = fp8_gemm_rowwise(dyt, sdyt, xt, sxt, out_dtype=dw_dtype)
+    return dx, dw

@@ -38,6 +38,10 @@ SIGNATURES = {
                                            ctypes.c_size_t, _P]),
     "fp8_block_gemm_workspace_bytes": (ctypes.c_size_t, [_I64, _I64, _I64, ctypes.c_int]),
     "fp8_grouped_gemm": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.c_int, _I64, _I64, _I64, _I64, _P]),
+    "fp8_act_quant_t": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _P]),
+    "fp8_weight_transpose": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _P]),
+    "fp8_rowwise_gemm": (ctypes.c_int, [_P, _P, _P, _P, _P, ctypes.c_int, _I64, _I64, _I64, _P, ctypes.c_size_t, _P]),
+    "fp8_rowwise_gemm_workspace_bytes": (ctypes.c_size_t, [_I64, _I64, _I64, ctypes.c_int]),
     "fp8q_gemm_force_config": (ctypes.c_int, [ctypes.c_int, ctypes.c_int]),
     "fp8q_gemm_config_name": (ctypes.c_char_p, [ctypes.c_int]),
     "fp8q_strerror": (ctypes.c_char_p, [ctypes.c_int]),

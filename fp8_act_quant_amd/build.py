@@ -12,7 +12,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfp8q.so")
 
-SOURCES = ["api.hip", "quant.hip", "gemm.hip"]
+SOURCES = ["api.hip", "quant.hip", "gemm.hip", "transpose.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

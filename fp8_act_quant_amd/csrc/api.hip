@@ -18,6 +18,8 @@ constexpr int64_t kMaxElems = (int64_t)1 << 46;
 constexpr int64_t kMaxWeightBlockRows = 65535;
 // the GEMM addresses a workgroup's rows of A and W with 32-bit offsets: K <= 2^24
 constexpr int64_t kMaxGemmK = (int64_t)1 << 24;
+// grid dimensions of the two-dimensional launches
+constexpr int64_t kMaxGridX = 0x7FFFFFFF, kMaxGridY = 65535;
 
 bool misaligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
 
@@ -136,6 +138,62 @@ int fp8_grouped_gemm(const uint8_t *aq, const float *sa, const uint8_t *wq, cons
                                             N, K, static_cast<hipStream_t>(stream)));
 }
 
+int fp8_act_quant_t(const uint16_t *x, uint8_t *qt, float *st, int64_t M, int64_t C, void *stream) {
+    if (M < 0 || C < 0 || (C % 8) != 0) return FP8Q_ERR_SHAPE;
+    const int64_t ldq = (M + kBlock - 1) / kBlock * kBlock;
+    if ((C > 0 && ldq > kMaxElems / C) || (C + 127) / 128 > kMaxGridY || ldq / kBlock > kMaxGridX) return FP8Q_ERR_SHAPE;
+    if (M == 0 || C == 0) return FP8Q_OK;
+    if (!x || !qt || !st) return FP8Q_ERR_NULL;
+    if (misaligned(x, 16) || misaligned(qt, 16) || misaligned(st, 4)) return FP8Q_ERR_ALIGN;
+    if (int e = check_device()) return e;
+    return finish(fp8q::launch_act_quant_t(x, qt, st, M, C, static_cast<hipStream_t>(stream)));
+}
+
+int fp8_weight_transpose(const uint8_t *wq, const float *sw, uint8_t *wqt, float *swt, int64_t N, int64_t K,
+                         void *stream) {
+    if (int e = shape_ok(N, K)) return e;
+    if ((N + 63) / 64 > kMaxGridY) return FP8Q_ERR_SHAPE;
+    if (N == 0 || K == 0) return FP8Q_OK;
+    if (!wq || !sw || !wqt || !swt) return FP8Q_ERR_NULL;
+    if (misaligned(wq, 16) || misaligned(wqt, 16) || misaligned(sw, 4) || misaligned(swt, 4)) return FP8Q_ERR_ALIGN;
+    if (int e = check_device()) return e;
+    return finish(fp8q::launch_weight_transpose(wq, sw, wqt, swt, N, K, static_cast<hipStream_t>(stream)));
+}
+
+int fp8_rowwise_gemm(const uint8_t *aq, const float *sa, const uint8_t *bq, const float *sb, void *y, int y_dtype,
+                     int64_t M, int64_t N, int64_t K, void *workspace, size_t workspace_bytes, void *stream) {
+    const int dtype = y_dtype & 0xFF;
+    const int mode = y_dtype & ~0xFF;
+    if (dtype != FP8Q_OUT_F32 && dtype != FP8Q_OUT_BF16) return FP8Q_ERR_DTYPE;
+    if (mode != 0 && mode != FP8Q_GEMM_FP8_PRODUCTS && mode != FP8Q_GEMM_EXACT_SLICES) return FP8Q_ERR_DTYPE;
+    if (int e = shape_ok(M, K)) return e;
+    if (int e = shape_ok(N, K)) return e;
+    if (M > 0 && N > kMaxElems / M) return FP8Q_ERR_SHAPE;
+    if (K > kMaxGemmK) return FP8Q_ERR_SHAPE;
+    if (M == 0 || N == 0) return FP8Q_OK;
+    if (!y) return FP8Q_ERR_NULL;
+    if (K > 0 && (!aq || !sa || !bq || !sb)) return FP8Q_ERR_NULL;
+    if (misaligned(aq, 16) || misaligned(bq, 16) || misaligned(y, 16) || misaligned(sa, 4) || misaligned(sb, 4))
+        return FP8Q_ERR_ALIGN;
+    if (workspace == nullptr) workspace_bytes = 0;
+    if (workspace_bytes && misaligned(workspace, 16)) return FP8Q_ERR_ALIGN;
+    if (int e = check_device()) return e;
+    const bool exact = mode == FP8Q_GEMM_EXACT_SLICES || (mode == 0 && dtype == FP8Q_OUT_F32);
+    return finish(fp8q::launch_rowwise_gemm(aq, sa, bq, sb, y, dtype == FP8Q_OUT_BF16, exact, M, N, K, workspace,
+                                            workspace_bytes, static_cast<hipStream_t>(stream)));
+}
+
+size_t fp8_rowwise_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int y_dtype) {
+    if (M <= 0 || N <= 0 || K <= 0 || (K % kBlock) != 0 || K > kMaxGemmK) return 0;
+    if (N > kMaxElems / M || shape_ok(M, K) || shape_ok(N, K)) return 0;
+    const int dtype = y_dtype & 0xFF;
+    const int mode = y_dtype & ~0xFF;
+    if (dtype != FP8Q_OUT_F32 && dtype != FP8Q_OUT_BF16) return 0;
+    if (mode != 0 && mode != FP8Q_GEMM_FP8_PRODUCTS && mode != FP8Q_GEMM_EXACT_SLICES) return 0;
+    const bool exact = mode == FP8Q_GEMM_EXACT_SLICES || (mode == 0 && dtype == FP8Q_OUT_F32);
+    return fp8q::gemm_workspace_bytes(M, N, K, dtype == FP8Q_OUT_BF16, exact, true);
+}
+
 size_t fp8_block_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int y_dtype) {
     if (M <= 0 || N <= 0 || K <= 0 || (K % kBlock) != 0 || K > kMaxGemmK) return 0;
     if (N > kMaxElems / M || shape_ok(M, K) || shape_ok(N, K)) return 0;
@@ -166,6 +224,6 @@ const char *fp8q_strerror(int status) {
     }
 }
 
-int fp8q_version(void) { return (1 << 16) | 1; }
+int fp8q_version(void) { return (1 << 16) | 2; }
 
 }  // extern "C"

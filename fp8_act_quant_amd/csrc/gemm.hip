@@ -78,13 +78,16 @@ __device__ __forceinline__ void static_for(F &&f) {
     static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-template <int BM, int BN, int NSTAGE, int NW>
+// ROWB: the second operand has one scale per row and slice (sw [N, K/128], the layout of
+// the activation scales) instead of one per 128-row block and slice.
+template <int BM, int BN, int NSTAGE, int NW, int ROWB = 0>
 struct GemmSmem {
     static_assert(BM % 64 == 0 && BN % 64 == 0 && BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "tile shape");
     static constexpr int A_BYTES = BM * G_SLICE;
     static constexpr int W_BYTES = BN * G_SLICE;
     static constexpr int SA_BYTES = BM * 4;
-    static constexpr int SW_BYTES = 64 * 4;   // weight scales of 64 N-blocks from the tile's first
+    // weight scales: of 64 N-blocks from the tile's first, or (ROWB) of every tile row
+    static constexpr int SW_BYTES = ROWB ? BN * 4 : 64 * 4;
     static constexpr int STAGE = A_BYTES + W_BYTES + SA_BYTES + SW_BYTES;
     static constexpr int DUMMY = STAGE * NSTAGE;   // 256-byte landing area of padding copies
     static constexpr int FLAG = DUMMY + 256;       // split-K "last to arrive" flag
@@ -93,7 +96,8 @@ struct GemmSmem {
     // 128 B), each scale instruction 256 B (64 rows of one fp32)
     static constexpr int A_INSTR = BM / (8 * NW), W_INSTR = BN / (8 * NW);
     static constexpr int SA_BLOCKS = BM / 64, SA_INSTR = (SA_BLOCKS + NW - 1) / NW;
-    static constexpr int IPW = A_INSTR + W_INSTR + SA_INSTR + 1;
+    static constexpr int SB_BLOCKS = BN / 64, SW_INSTR = ROWB ? (SB_BLOCKS + NW - 1) / NW : 1;
+    static constexpr int IPW = A_INSTR + W_INSTR + SA_INSTR + SW_INSTR;
     static_assert((NSTAGE - 1) * IPW < 64, "vmcnt range");
 };
 
@@ -154,6 +158,13 @@ __device__ __forceinline__ void promote(f32x4 &acc, const f32x4 &p, float f) {
     asm volatile("" : "+v"(acc));
 }
 
+// acc += p * f per element, with one factor per element (per-row scales on both operands)
+__device__ __forceinline__ void promote(f32x4 &acc, const f32x4 &p, const f32x4 &f) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[r] = __builtin_fmaf(p[r], f[r], acc[r]);
+    asm volatile("" : "+v"(acc));
+}
+
 // wait for every outstanding LDS read (lgkmcnt 0; vmcnt and expcnt left alone)
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14)); }
 
@@ -207,12 +218,14 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *p, int64_t bytes) {
 // area. The weight-scale instruction copies the scales of the (at most 3) N-blocks the tile
 // spans, lane = N-block; the other lanes repeat lane 0's address, so they add no line
 // requests. (Each scale instruction addresses one line per active distinct row, so these
-// paddings would otherwise cost as many line requests as the tile rows themselves.)
+// paddings would otherwise cost as many line requests as the tile rows themselves.) With
+// per-row weight scales (ROWB) the weight-scale instructions copy 64 tile rows each, like
+// the activation-scale instructions.
 // VARIANT makes the type unique to each kernel instantiation: when kernels of different
 // variants shared one DmaPlan type, the host compiler emitted a launch stub for only one of them.
-template <int BM, int BN, int NSTAGE, int NW, int VARIANT, int NG>
+template <int BM, int BN, int NSTAGE, int NW, int VARIANT, int NG, int ROWB>
 struct DmaPlan {
-    using S = GemmSmem<BM, BN, NSTAGE, NW>;
+    using S = GemmSmem<BM, BN, NSTAGE, NW, ROWB>;
     rsrc_t ra, rw, rsa, rsw;
     uint32_t off[S::IPW];
     int w;
@@ -226,8 +239,12 @@ struct DmaPlan {
         ra = make_rsrc(aq + m0 * K, rows_a * K);
         rw = make_rsrc(wq + n0 * K, rows_w * K);
         rsa = make_rsrc(sa + m0 * nkb, rows_a * nkb * 4);
-        const int64_t nb0 = n0 / G_SLICE, nnb = (N + G_SLICE - 1) / G_SLICE;
-        rsw = make_rsrc(sw + nb0 * nkb, (nnb - nb0) * nkb * 4);
+        if constexpr (ROWB) {
+            rsw = make_rsrc(sw + n0 * nkb, rows_w * nkb * 4);
+        } else {
+            const int64_t nb0 = n0 / G_SLICE, nnb = (N + G_SLICE - 1) / G_SLICE;
+            rsw = make_rsrc(sw + nb0 * nkb, (nnb - nb0) * nkb * 4);
+        }
         w = wave;
         dummy = smem_dummy;
         const int sub = lane >> 3;
@@ -246,7 +263,15 @@ struct DmaPlan {
             const int b = NW * t + w;
             off[S::A_INSTR + S::W_INSTR + t] = b < S::SA_BLOCKS ? (uint32_t)((64 * b + lane) * nkb * 4) : 0u;
         }
-        off[S::IPW - 1] = (uint32_t)((lane < 4 ? lane : 0) * nkb * 4);
+        if constexpr (ROWB) {
+#pragma unroll
+            for (int t = 0; t < S::SW_INSTR; ++t) {
+                const int b = NW * t + w;
+                off[S::IPW - S::SW_INSTR + t] = b < S::SB_BLOCKS ? (uint32_t)((64 * b + lane) * nkb * 4) : 0u;
+            }
+        } else {
+            off[S::IPW - 1] = (uint32_t)((lane < 4 ? lane : 0) * nkb * 4);
+        }
     }
 
     // instruction I (of IPW) of the copies of slice kb into stage buffer `base`; I is a
@@ -259,10 +284,14 @@ struct DmaPlan {
             const int t = I - S::A_INSTR;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void *)(base + S::A_BYTES + 8 * (NW * t + w) * G_SLICE),
                                                      16, off[I], koff, 0, 0);
-        } else if (I < S::IPW - 1) {
+        } else if (I < S::IPW - S::SW_INSTR) {
             const int b = NW * (I - S::A_INSTR - S::W_INSTR) + w;
             uint8_t *dst = b < S::SA_BLOCKS ? base + S::A_BYTES + S::W_BYTES + b * 256 : dummy;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_void *)dst, 4, off[I], soff, 0, 0);
+        } else if (ROWB) {
+            const int b = NW * (I - (S::IPW - S::SW_INSTR)) + w;
+            uint8_t *dst = b < S::SB_BLOCKS ? base + S::A_BYTES + S::W_BYTES + S::SA_BYTES + b * 256 : dummy;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsw, (lds_void *)dst, 4, off[I], soff, 0, 0);
         } else {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rsw, (lds_void *)(base + S::A_BYTES + S::W_BYTES + S::SA_BYTES),
                                                      4, off[I], soff, 0, 0);
@@ -384,9 +413,10 @@ __device__ __forceinline__ bool grouped_tile(const GemmArgs &g, uint8_t *scratch
     return true;
 }
 
-template <int BM, int BN, int NW, int WAVES_M, int NSTAGE, int OUT_BF16, int EXACT, int GROUPED>
+template <int BM, int BN, int NW, int WAVES_M, int NSTAGE, int OUT_BF16, int EXACT, int GROUPED, int ROWB>
 __global__ __launch_bounds__(NW * 64) void block_gemm_kernel(GemmArgs g) {
-    using S = GemmSmem<BM, BN, NSTAGE, NW>;
+    static_assert(!(GROUPED && ROWB), "per-row weight scales are not grouped");
+    using S = GemmSmem<BM, BN, NSTAGE, NW, ROWB>;
     constexpr int WAVES_N = NW / WAVES_M;
     static_assert(WAVES_M * WAVES_N == NW, "wave grid");
     constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;    // wave tile
@@ -469,7 +499,7 @@ __global__ __launch_bounds__(NW * 64) void block_gemm_kernel(GemmArgs g) {
         // wait of wait_slice covers exactly the next slice.
         constexpr int COPY_PARTS = EARLY_BARRIER ? SUB_M - 1 : SUB_M;
         static_assert(COPY_PARTS >= 1, "row groups per wave");
-        const DmaPlan<BM, BN, NSTAGE, NW, GROUPED * 4 + OUT_BF16 * 2 + EXACT, COPY_PARTS> dma(wave, lane, g.aq, wq, g.sa, sw, m0, n0, M, N,
+        const DmaPlan<BM, BN, NSTAGE, NW, ROWB * 8 + GROUPED * 4 + OUT_BF16 * 2 + EXACT, COPY_PARTS, ROWB> dma(wave, lane, g.aq, wq, g.sa, sw, m0, n0, M, N,
                                                                    K, nkb, smem + S::DUMMY);
         // prologue: the first NSTAGE slices in flight
 #pragma unroll
@@ -488,13 +518,16 @@ __global__ __launch_bounds__(NW * 64) void block_gemm_kernel(GemmArgs g) {
         int a_lo = wm * WM * G_SLICE + frag_lo, a_hi = wm * WM * G_SLICE + frag_hi;
         int w_lo = S::A_BYTES + wn * WN * G_SLICE + frag_lo, w_hi = S::A_BYTES + wn * WN * G_SLICE + frag_hi;
         int sa_at = S::A_BYTES + S::W_BYTES + (wm * WM + frow) * 4;
+        // weight scale of each n-subtile: of its N-block, or (ROWB) of this lane's four columns
         int sw_at[SUB_N];
 #pragma unroll
-        for (int j = 0; j < SUB_N; ++j) sw_at[j] = S::A_BYTES + S::W_BYTES + S::SA_BYTES + sw_idx[ONE_SW ? 0 : j] * 4;
+        for (int j = 0; j < SUB_N; ++j)
+            sw_at[j] = S::A_BYTES + S::W_BYTES + S::SA_BYTES +
+                       (ROWB ? (wn * WN + 16 * j + 4 * kgroup) * 4 : sw_idx[ONE_SW ? 0 : j] * 4);
         if constexpr (NW == 8) {   // (the 4-wave tiles are short of registers: offsets recomputed there)
             asm volatile("" : "+v"(a_lo), "+v"(a_hi), "+v"(w_lo), "+v"(w_hi), "+v"(sa_at));
 #pragma unroll
-            for (int j = 0; j < (ONE_SW ? 1 : SUB_N); ++j) asm volatile("" : "+v"(sw_at[j]));
+            for (int j = 0; j < (ONE_SW && !ROWB ? 1 : SUB_N); ++j) asm volatile("" : "+v"(sw_at[j]));
         }
         auto frag_at = [&](const uint8_t *base, int lo, int hi) __device__ __attribute__((always_inline)) {
             const u32x4 l = *reinterpret_cast<const u32x4 *>(base + lo);
@@ -504,11 +537,20 @@ __global__ __launch_bounds__(NW * 64) void block_gemm_kernel(GemmArgs g) {
         auto f32_at = [&](const uint8_t *base, int off) __device__ __attribute__((always_inline)) {
             return *reinterpret_cast<const float *>(base + off);
         };
+        // weight scale(s) of n-subtile j: one float, or (ROWB) the four of this lane's columns
+        using WScale = std::conditional_t<ROWB != 0, f32x4, float>;
+        constexpr bool ONE_WS = ONE_SW && !ROWB;
+        auto ws_at = [&](const uint8_t *base, int j) __device__ __attribute__((always_inline)) {
+            if constexpr (ROWB != 0)
+                return *reinterpret_cast<const f32x4 *>(base + sw_at[j]);
+            else
+                return *reinterpret_cast<const float *>(base + sw_at[ONE_WS ? 0 : j]);
+        };
 
         // fragments of the slice being contracted
         i32x8 wf[SUB_N];
         Frag16 wh[EXACT ? SUB_N : 1];
-        float swv[SUB_N];
+        WScale swv[SUB_N];
         i32x8 af;
         float sav;
         auto load_slice_head = [&](const uint8_t *stage) __device__ __attribute__((always_inline)) {
@@ -517,7 +559,7 @@ __global__ __launch_bounds__(NW * 64) void block_gemm_kernel(GemmArgs g) {
             af = frag_at(stage, a_lo, a_hi);
             sav = f32_at(stage, sa_at);
 #pragma unroll
-            for (int j = 0; j < SUB_N; ++j) swv[j] = f32_at(stage, sw_at[ONE_SW ? 0 : j]);
+            for (int j = 0; j < SUB_N; ++j) swv[j] = ws_at(stage, j);
             if constexpr (EXACT) {
 #pragma unroll
                 for (int j = 0; j < SUB_N; ++j) wh[j] = to_f16(wf[j]);
@@ -528,11 +570,11 @@ __global__ __launch_bounds__(NW * 64) void block_gemm_kernel(GemmArgs g) {
         // promotion of each row group runs one group behind its MFMAs (the last group of a
         // slice is promoted during the first group of the next); it starts from a zero partial
         f32x4 p_prev[SUB_N];
-        float f_prev[SUB_N];
+        WScale f_prev[SUB_N];
 #pragma unroll
         for (int j = 0; j < SUB_N; ++j) {
             p_prev[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-            f_prev[j] = 0.f;
+            f_prev[j] = WScale{};
         }
         // With 8 waves the K loop is unrolled by NSTAGE: each slice's stage buffer, the buffer
         // its copies go to and the next slice's buffer are then compile-time offsets, so
@@ -575,12 +617,12 @@ __global__ __launch_bounds__(NW * 64) void block_gemm_kernel(GemmArgs g) {
                     af_n = frag_at(stage + 16 * (i + 1) * G_SLICE, a_lo, a_hi);
                     sav_n = f32_at(stage + 16 * (i + 1) * 4, sa_at);
                 }
-                float f_cur[SUB_N];
+                WScale f_cur[SUB_N];
 #pragma unroll
-                for (int j = 0; j < SUB_N; ++j) f_cur[j] = sav * (ONE_SW ? swv[0] : swv[j]);
+                for (int j = 0; j < SUB_N; ++j) f_cur[j] = sav * swv[ONE_WS ? 0 : j];
                 if (head_now) {
 #pragma unroll
-                    for (int j = 0; j < SUB_N; ++j) swv[j] = f32_at(next, sw_at[ONE_SW ? 0 : j]);
+                    for (int j = 0; j < SUB_N; ++j) swv[j] = ws_at(next, j);
                 }
                 f32x4 p_cur[SUB_N];
                 const int ip = i == 0 ? SUB_M - 1 : i - 1;   // row group being promoted (a constant once unrolled)
@@ -801,13 +843,18 @@ struct TileInfo {
     bool fp8_ok, exact_ok;
     double us_slice, us_fixed;       // FP8-product mode
     double us_slice_x, us_fixed_x;   // exact-slice mode (0: not implemented)
+    int rowb_ok;                     // instantiated with per-row weight scales: 1 FP8 mode, 2 exact mode
 };
 
 static const TileInfo kTiles[T_COUNT] = {
-    {"256x256w8", 256, 256, true, false, 1.84, 10.0, 0, 0},      {"256x192w8", 256, 192, true, false, 1.59, 7.5, 0, 0},
-    {"256x128w8", 256, 128, true, true, 1.02, 7.0, 2.04, 5.9},   {"128x256w8", 128, 256, true, true, 0.94, 7.0, 2.10, 4.7},
-    {"128x192w8", 128, 192, true, true, 0.78, 5.9, 1.61, 4.7},   {"256x128", 256, 128, true, false, 1.22, 7.1, 0, 0},
-    {"128x128", 128, 128, true, true, 0.82, 4.4, 1.36, 4.6},     {"128x128s2", 128, 128, false, false, 0.95, 2.8, 0, 0},
+    {"256x256w8", 256, 256, true, false, 1.84, 10.0, 0, 0, 0},
+    {"256x192w8", 256, 192, true, false, 1.59, 7.5, 0, 0, 0},
+    {"256x128w8", 256, 128, true, true, 1.02, 7.0, 2.04, 5.9, 1},
+    {"128x256w8", 128, 256, true, true, 0.94, 7.0, 2.10, 4.7, 1},
+    {"128x192w8", 128, 192, true, true, 0.78, 5.9, 1.61, 4.7, 3},
+    {"256x128", 256, 128, true, false, 1.22, 7.1, 0, 0, 0},
+    {"128x128", 128, 128, true, true, 0.82, 4.4, 1.36, 4.6, 3},
+    {"128x128s2", 128, 128, false, false, 0.95, 2.8, 0, 0, 0},
 };
 
 constexpr int kNumCUs = 256;
@@ -905,7 +952,8 @@ static double plan_cost(int tile, int64_t tiles, int splits, int64_t nkb, bool e
     return waves * per_unit + (splits - 1) * 0.23 * kouts;
 }
 
-static GemmPlan make_plan(int64_t M, int64_t N, int64_t K, bool exact, size_t ws_bytes, bool size_query) {
+static GemmPlan make_plan(int64_t M, int64_t N, int64_t K, bool exact, size_t ws_bytes, bool size_query,
+                          bool rowb = false) {
     const int64_t nkb = K / G_SLICE;
     GemmPlan best{T128x128, 1, (M + 127) / 128, (N + 127) / 128};
     double best_cost = 1e300;
@@ -913,6 +961,8 @@ static GemmPlan make_plan(int64_t M, int64_t N, int64_t K, bool exact, size_t ws
     for (int t = 0; t < T_COUNT; ++t) {
         // a forced tile (tuning) is taken even where the planner would not pick it
         if (forced_tile >= 0 ? t != forced_tile : (exact ? !kTiles[t].exact_ok : !kTiles[t].fp8_ok)) continue;
+        // (a forced tile without it leaves the default)
+        if (rowb && !(kTiles[t].rowb_ok & (exact ? 2 : 1))) continue;
         const int64_t tm = (M + kTiles[t].bm - 1) / kTiles[t].bm, tn = (N + kTiles[t].bn - 1) / kTiles[t].bn;
         for (int s = 1; s <= (exact ? 1 : kMaxSplits); ++s) {
             // a split contracts at least 2 slices; a forced count falls back to 1 where it cannot apply
@@ -931,11 +981,11 @@ static GemmPlan make_plan(int64_t M, int64_t N, int64_t K, bool exact, size_t ws
     return best;
 }
 
-size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, bool, bool exact) {
-    return split_bytes(make_plan(M, N, K, exact, 0, true));
+size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, bool, bool exact, bool rowb) {
+    return split_bytes(make_plan(M, N, K, exact, 0, true, rowb));
 }
 
-template <int BM, int BN, int NW, int WAVES_M, int NSTAGE, int EXACT, int GROUPED = 0>
+template <int BM, int BN, int NW, int WAVES_M, int NSTAGE, int EXACT, int GROUPED = 0, int ROWB = 0>
 static hipError_t launch_cfg(GemmArgs a, bool out_bf16, int splits, hipStream_t stream) {
     // grouped: an upper bound on the m-tiles of all experts (sum of ceil(rows_e / BM))
     a.tiles_m = (int)((a.M + BM - 1) / BM + (a.offsets ? a.experts : 0));
@@ -944,9 +994,9 @@ static hipError_t launch_cfg(GemmArgs a, bool out_bf16, int splits, hipStream_t 
     a.splits = splits;
     const dim3 grid((unsigned)((int64_t)a.tiles_m * a.tiles_n * splits)), block(NW * 64);
     if (out_bf16)
-        block_gemm_kernel<BM, BN, NW, WAVES_M, NSTAGE, 1, EXACT, GROUPED><<<grid, block, 0, stream>>>(a);
+        block_gemm_kernel<BM, BN, NW, WAVES_M, NSTAGE, 1, EXACT, GROUPED, ROWB><<<grid, block, 0, stream>>>(a);
     else
-        block_gemm_kernel<BM, BN, NW, WAVES_M, NSTAGE, 0, EXACT, GROUPED><<<grid, block, 0, stream>>>(a);
+        block_gemm_kernel<BM, BN, NW, WAVES_M, NSTAGE, 0, EXACT, GROUPED, ROWB><<<grid, block, 0, stream>>>(a);
     return hipGetLastError();
 }
 
@@ -969,6 +1019,35 @@ static hipError_t dispatch(const GemmPlan &p, const GemmArgs &a, bool out_bf16, 
     case T128x128S2: return launch_cfg<128, 128, 4, 2, 2, 0>(a, out_bf16, p.splits, stream);
     default: return launch_cfg<128, 128, 4, 2, 4, 0>(a, out_bf16, p.splits, stream);
     }
+}
+
+// per-row weight scales: the subset of tiles instantiated for them
+static hipError_t dispatch_rowb(const GemmPlan &p, const GemmArgs &a, bool out_bf16, bool exact, hipStream_t stream) {
+    if (exact) {
+        switch (p.tile) {
+        case T128x192W8: return launch_cfg<128, 192, 8, 2, 3, 1, 0, 1>(a, out_bf16, 1, stream);
+        default: return launch_cfg<128, 128, 4, 2, 4, 1, 0, 1>(a, out_bf16, 1, stream);
+        }
+    }
+    switch (p.tile) {
+    case T256x128W8: return launch_cfg<256, 128, 8, 4, 3, 0, 0, 1>(a, out_bf16, p.splits, stream);
+    case T128x256W8: return launch_cfg<128, 256, 8, 2, 3, 0, 0, 1>(a, out_bf16, p.splits, stream);
+    case T128x192W8: return launch_cfg<128, 192, 8, 2, 3, 0, 0, 1>(a, out_bf16, p.splits, stream);
+    default: return launch_cfg<128, 128, 4, 2, 4, 0, 0, 1>(a, out_bf16, p.splits, stream);
+    }
+}
+
+hipError_t launch_rowwise_gemm(const uint8_t *aq, const float *sa, const uint8_t *bq, const float *sb, void *y,
+                               bool out_bf16, bool exact, int64_t M, int64_t N, int64_t K, void *workspace,
+                               size_t workspace_bytes, hipStream_t stream) {
+    if (M == 0 || N == 0) return hipSuccess;
+    const GemmPlan p = make_plan(M, N, K, exact, workspace ? workspace_bytes : 0, false, true);
+    GemmArgs a{aq, sa, bq, sb, y, nullptr, nullptr, nullptr, nullptr, M, N, K, 0, 0, 1, 1, 0};
+    if (p.splits > 1) {
+        a.count = static_cast<uint32_t *>(workspace);
+        a.part = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + kCounterBytes);
+    }
+    return dispatch_rowb(p, a, out_bf16, exact, stream);
 }
 
 hipError_t launch_block_gemm(const uint8_t *aq, const float *sa, const uint8_t *wq, const float *sw,

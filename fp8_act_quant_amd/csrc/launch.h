@@ -23,7 +23,22 @@ hipError_t launch_weight_dequant(const uint8_t *q, const float *s, uint16_t *w, 
 hipError_t launch_block_gemm(const uint8_t *aq, const float *sa, const uint8_t *wq, const float *sw,
                              const float *bias, void *y, bool out_bf16, bool exact, int64_t M, int64_t N,
                              int64_t K, void *workspace, size_t workspace_bytes, hipStream_t stream);
-size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, bool out_bf16, bool exact);
+size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, bool out_bf16, bool exact, bool rowb = false);
+
+// GEMM with per-row scales on both operands: Y = sum over slices kb of
+// (sum_k aq[m,k] bq[n,k]) * sa[m,kb] * sb[n,kb], sb [N, K/128]. Otherwise as launch_block_gemm
+// (no bias); its workspace size is gemm_workspace_bytes(..., rowb = true).
+hipError_t launch_rowwise_gemm(const uint8_t *aq, const float *sa, const uint8_t *bq, const float *sb, void *y,
+                               bool out_bf16, bool exact, int64_t M, int64_t N, int64_t K, void *workspace,
+                               size_t workspace_bytes, hipStream_t stream);
+
+// Training-side layout kernels. act_quant_t: x [M, C] bf16 -> qt [C, ldq] E4M3 and
+// st [C, ldq / 128], ldq = ceil(M / 128) * 128: the 1x128 tiles run along the token
+// dimension (column tiles of x), tokens past M are zero. weight_transpose: wq [N, K] ->
+// wqt [K, N], sw [ceil(N/128), K/128] -> swt [K/128, ceil(N/128)].
+hipError_t launch_act_quant_t(const uint16_t *x, uint8_t *qt, float *st, int64_t M, int64_t C, hipStream_t stream);
+hipError_t launch_weight_transpose(const uint8_t *wq, const float *sw, uint8_t *wqt, float *swt, int64_t N,
+                                   int64_t K, hipStream_t stream);
 
 // Grouped GEMM over `experts` weight matrices: expert e multiplies rows [offsets[e],
 // offsets[e+1]) of A (device int64 offsets, clamped to [0, rows]) by wq + e*N*K.

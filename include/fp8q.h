@@ -166,6 +166,43 @@ int fp8_grouped_gemm(const uint8_t *aq, const float *sa, const uint8_t *wq, cons
                      const int64_t *offsets, void *y, int y_dtype, int64_t experts, int64_t rows,
                      int64_t N, int64_t K, void *stream);
 
+/* ---- Training GEMMs (backward of linear()) -------------------------------------------
+ * The pages train in FP8 with E4M3 everywhere (88811315.cn post 75335, Float8-training
+ * paragraph; pomoai.com "DeepSeek-V3", "FP8 mixed-precision training") but give the
+ * backward pass's granularity nowhere. Reading taken here: each GEMM operand is quantised
+ * by the forward rules along its contraction dimension. For y = x W^T:
+ *   activation gradient dX [M, K] = dY [M, N] . W [N, K]: dY by fp8_act_quant (1x128 tiles
+ *     along N); W's 128x128 blocks are square, so W^T has the same codes and block scales,
+ *     transposed (fp8_weight_transpose), and dX = fp8_block_gemm(dYq, sdy, Wq^T, sw^T).
+ *   weight gradient dW [N, K] = dY^T . X, contracted over tokens: dY and X both quantised in
+ *     1x128 tiles along the token dimension (fp8_act_quant_t), and
+ *     dW = fp8_rowwise_gemm(dY^T q, s, X^T q, s) with per-row scales on both operands. */
+
+/* fp8_act_quant_t -- token-wise quantisation with a transposed output.
+ *   x [M, C] bf16 (row-major; C a multiple of 8).
+ *   qt [C, ldq] E4M3 and st [C, ldq/128] fp32, ldq = ceil(M/128)*128: row c holds channel c
+ *      over all tokens; the tile (c, mb) covers tokens 128 mb .. 128 mb + 127 and follows
+ *      fp8_act_quant's rules (amax over the tile, s = RN(amax/448), RNE-saturated codes).
+ *      Tokens M .. ldq-1 are written as code 0 and enter no amax, so qt can be contracted
+ *      over ldq directly.
+ *   Alignment: x, qt 16 bytes; st 4. M or C = 0: no-op. */
+int fp8_act_quant_t(const uint16_t *x, uint8_t *qt, float *st, int64_t M, int64_t C, void *stream);
+
+/* fp8_weight_transpose -- Wq [N, K] E4M3 -> Wq^T [K, N]; sw [ceil(N/128), K/128] ->
+ *   sw^T [K/128, ceil(N/128)]. K a multiple of 128; any N >= 0 (a contraction over N in a
+ *   block GEMM needs N to be a multiple of 128). wq, wqt 16-byte aligned; sw, swt 4. */
+int fp8_weight_transpose(const uint8_t *wq, const float *sw, uint8_t *wqt, float *swt, int64_t N, int64_t K,
+                         void *stream);
+
+/* fp8_rowwise_gemm -- Y [M, N] = sum over slices kb of P[m,n,kb] * sa[m,kb] * sb[n,kb],
+ *   P the exact contraction of 128-wide K slice kb of aq [M, K] and bq [N, K] (both E4M3,
+ *   K-contiguous), sa [M, K/128], sb [N, K/128] fp32: fp8_block_gemm with a per-row scale on
+ *   the second operand instead of a 128x128 block scale. y_dtype, modes, workspace (size from
+ *   fp8_rowwise_gemm_workspace_bytes), alignment and errors as for fp8_block_gemm; no bias. */
+int fp8_rowwise_gemm(const uint8_t *aq, const float *sa, const uint8_t *bq, const float *sb, void *y, int y_dtype,
+                     int64_t M, int64_t N, int64_t K, void *workspace, size_t workspace_bytes, void *stream);
+size_t fp8_rowwise_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int y_dtype);
+
 /* Workspace size in bytes that lets fp8_block_gemm use its split-K schedule for this
  * shape and y_dtype (including the mode bits); 0 if that call does not use one or the
  * arguments are invalid. Host-only; enqueues nothing. */

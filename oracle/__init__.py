@@ -59,6 +59,8 @@ def _load():
         "or_block_gemm": (None, [P, P, P, P, I64, I64, I64, P, P]),
         "or_block_gemm_sampled": (None, [P, P, P, P, I64, I64, I64, P, P, I64, P, P]),
         "or_matmul_bf16_sampled": (None, [P, P, I64, P, P, I64, P]),
+        "or_rowwise_gemm": (None, [P, P, P, P, I64, I64, I64, P, P]),
+        "or_rowwise_gemm_sampled": (None, [P, P, P, P, I64, P, P, I64, P, P]),
         "or_e4m3_encode_batch": (None, [P, P, I64]),
         "or_f32_to_bf16_batch": (None, [P, P, I64]),
         "or_f64_to_bf16_batch": (None, [P, P, I64]),
@@ -154,6 +156,25 @@ def weight_quant(w_bf16: np.ndarray):
     return q, s
 
 
+def act_quant_t(x_bf16: np.ndarray):
+    """Token-wise quantisation for the weight gradient (the 1x128 activation rule applied
+    along the token dimension): x uint16 (bf16 bits) [M, C] -> (qt uint8 [C, ldq],
+    st float32 [C, ldq/128]), ldq = ceil(M/128)*128. The tokens are zero-padded to ldq and
+    the transposed matrix goes through act_quant (a zero token enters no amax and encodes to
+    code 0)."""
+    x = _c(x_bf16, np.uint16)
+    M, C = x.shape
+    ldq = -(-M // BLOCK) * BLOCK
+    xt = np.zeros((C, ldq), dtype=np.uint16)
+    xt[:, :M] = x.T
+    return act_quant(xt)
+
+
+def weight_transpose(q: np.ndarray, s: np.ndarray):
+    """Wq [N, K] -> Wq^T [K, N]; scale grid [ceil(N/128), K/128] -> its transpose."""
+    return np.ascontiguousarray(np.asarray(q, dtype=np.uint8).T), np.ascontiguousarray(np.asarray(s, np.float32).T)
+
+
 def weight_dequant(q: np.ndarray, s: np.ndarray) -> np.ndarray:
     """q: uint8 [N, K], s: float32 [ceil(N/128), K/128] -> uint16 (bf16 bits) [N, K]."""
     q = _c(q, np.uint8)
@@ -235,6 +256,41 @@ def grouped_gemm(aq, sa, wq, sw, offsets):
         r0, r1 = offsets[e], offsets[e + 1]
         if r1 > r0:
             y[r0:r1], b[r0:r1] = block_gemm(aq[r0:r1], sa[r0:r1], wq[e], sw[e])
+    return y, b
+
+
+def rowwise_gemm(aq, sa, bq, sb):
+    """GEMM with per-row scales on both operands (sb [N, K/128]): full float64 result and
+    bound (y [M, N], bound [M, N])."""
+    aq, bq = _c(aq, np.uint8), _c(bq, np.uint8)
+    sa, sb = _c(sa, np.float32), _c(sb, np.float32)
+    M, K = aq.shape
+    N = bq.shape[0]
+    if bq.shape[1] != K or K % BLOCK or sa.shape != (M, K // BLOCK) or sb.shape != (N, K // BLOCK):
+        raise ValueError("shape mismatch")
+    y = np.empty((M, N), dtype=np.float64)
+    b = np.empty((M, N), dtype=np.float64)
+    _load().or_rowwise_gemm(_ptr(aq), _ptr(sa), _ptr(bq), _ptr(sb), M, N, K, _ptr(y), _ptr(b))
+    return y, b
+
+
+def rowwise_gemm_sampled(aq, sa, bq, sb, rows, cols):
+    """rowwise_gemm at outputs (rows[i], cols[i])."""
+    aq, bq = _c(aq, np.uint8), _c(bq, np.uint8)
+    sa, sb = _c(sa, np.float32), _c(sb, np.float32)
+    M, K = aq.shape
+    N = bq.shape[0]
+    if bq.shape[1] != K or K % BLOCK or sa.shape != (M, K // BLOCK) or sb.shape != (N, K // BLOCK):
+        raise ValueError("shape mismatch")
+    rows = _c(np.asarray(rows, dtype=np.int64), np.int64)
+    cols = _c(np.asarray(cols, dtype=np.int64), np.int64)
+    if rows.shape != cols.shape or (rows.size and (rows.min() < 0 or rows.max() >= M or cols.min() < 0
+                                                   or cols.max() >= N)):
+        raise ValueError("bad sample coordinates")
+    y = np.empty(rows.shape, dtype=np.float64)
+    b = np.empty(rows.shape, dtype=np.float64)
+    _load().or_rowwise_gemm_sampled(_ptr(aq), _ptr(sa), _ptr(bq), _ptr(sb), K, _ptr(rows), _ptr(cols), rows.size,
+                                    _ptr(y), _ptr(b))
     return y, b
 
 

@@ -312,6 +312,56 @@ void or_block_gemm_sampled(const uint8_t *aq, const float *sa, const uint8_t *wq
         gemm_one(dec, aq, sa, wq, sw, N, K, rows[i], cols[i], y + i, bound + i);
 }
 
+/* ---------------------------------------------------------------------------------
+ * GEMM with per-row scales on both operands (the weight-gradient reading: both operands
+ * quantised in 1x128 tiles along the contraction dimension). For output (m, n):
+ *   P_kb = sum_{k in slice kb} decode(aq[m,k]) * decode(bq[n,k])   (exact, as above)
+ *   y    = sum_kb P_kb * (sa[m, kb] * sb[n, kb]),  bound = sum_kb |P|_kb * |sa * sb|.
+ * With sb rows equal within each 128-row block this is or_block_gemm.
+ * ------------------------------------------------------------------------------- */
+static void rowwise_one(const double *dec, const uint8_t *aq, const float *sa, const uint8_t *bq,
+                        const float *sb, int64_t K, int64_t m, int64_t n, double *y_out,
+                        double *bound_out)
+{
+    int64_t nkb = K / OR_BLOCK;
+    const uint8_t *arow = aq + m * K;
+    const uint8_t *brow = bq + n * K;
+    double y = 0.0, bound = 0.0;
+    for (int64_t kb = 0; kb < nkb; ++kb) {
+        double p = 0.0, pabs = 0.0;
+        for (int64_t k = kb * OR_BLOCK; k < (kb + 1) * OR_BLOCK; ++k) {
+            double t = dec[arow[k]] * dec[brow[k]];
+            p += t;
+            pabs += fabs(t);
+        }
+        double f = (double)sa[m * nkb + kb] * (double)sb[n * nkb + kb];
+        y += p * f;
+        bound += pabs * fabs(f);
+    }
+    *y_out = y;
+    *bound_out = bound;
+}
+
+void or_rowwise_gemm(const uint8_t *aq, const float *sa, const uint8_t *bq, const float *sb,
+                     int64_t M, int64_t N, int64_t K, double *y, double *bound)
+{
+    const double *dec = e4m3_value;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n)
+            rowwise_one(dec, aq, sa, bq, sb, K, m, n, y + m * N + n, bound + m * N + n);
+}
+
+void or_rowwise_gemm_sampled(const uint8_t *aq, const float *sa, const uint8_t *bq,
+                             const float *sb, int64_t K, const int64_t *rows,
+                             const int64_t *cols, int64_t count, double *y, double *bound)
+{
+    const double *dec = e4m3_value;
+#pragma omp parallel for schedule(dynamic, 64)
+    for (int64_t i = 0; i < count; ++i)
+        rowwise_one(dec, aq, sa, bq, sb, K, rows[i], cols[i], y + i, bound + i);
+}
+
 /* Unquantised float64 product of the original bf16 operands at sampled outputs, for the
  * informational relative error of the FP8 path: y[i] = sum_k x[r,k] * w[c,k]. */
 void or_matmul_bf16_sampled(const uint16_t *x, const uint16_t *w, int64_t K, const int64_t *rows,

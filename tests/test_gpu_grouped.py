@@ -215,3 +215,28 @@ def test_grouped_error_paths():
         fq.fp8_grouped_gemm(a.view(torch.float8_e4m3fn), s, w.view(torch.float8_e4m3fn), ws, off[:2])
     with pytest.raises(TypeError):
         fq.fp8_grouped_gemm(a.view(torch.float8_e4m3fn), s, w.view(torch.float8_e4m3fn), ws, off[:3].int())
+
+
+def test_grouped_and_plain_repeat_bitwise_at_full_size():
+    """Repeated launches give identical bits (no race between the copies into a stage buffer
+    and the reads of it): the routed down-projection with every local expert, and the plain
+    GEMM on the q_down shape, each run three times on the same inputs."""
+    wl = synth.MOE_WORKLOADS["moe_down"]
+    _, offsets = synth.moe_routing(wl)
+    R, E, N, K = int(offsets[-1]), wl.local_experts, wl.N, wl.K
+    g = torch.Generator(device="cuda").manual_seed(5)
+    aq, sa = fq.act_quant(torch.randn((R, K), generator=g, device="cuda").to(torch.bfloat16))
+    wq = torch.empty((E, N, K), dtype=torch.float8_e4m3fn, device="cuda")
+    sw = torch.empty((E, N // 128, K // 128), dtype=torch.float32, device="cuda")
+    for e in range(E):
+        wq[e], sw[e] = fq.weight_quant((torch.randn((N, K), generator=g, device="cuda") * 0.02).to(torch.bfloat16))
+    off = torch.from_numpy(offsets).cuda()
+    ys = [fq.fp8_grouped_gemm(aq, sa, wq, sw, off).view(torch.int16) for _ in range(3)]
+    torch.cuda.synchronize()
+    assert all(torch.equal(ys[0], y) for y in ys[1:]), [int((ys[0] != y).sum()) for y in ys[1:]]
+    M, N, K = 4096, 1536, 7168
+    aq, sa = fq.act_quant(torch.randn((M, K), generator=g, device="cuda").to(torch.bfloat16))
+    wq, sw = fq.weight_quant((torch.randn((N, K), generator=g, device="cuda") * 0.02).to(torch.bfloat16))
+    ys = [fq.fp8_gemm(aq, sa, wq, sw).view(torch.int16) for _ in range(3)]
+    torch.cuda.synchronize()
+    assert all(torch.equal(ys[0], y) for y in ys[1:]), [int((ys[0] != y).sum()) for y in ys[1:]]

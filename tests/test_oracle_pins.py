@@ -558,3 +558,111 @@ def test_moe_routing_is_a_valid_grouping():
     assert np.diff(offsets).max() > 2 * np.diff(offsets).min()
     tok2, off2 = synth.moe_routing(wl, seed=0)
     assert np.array_equal(tok, tok2) and np.array_equal(offsets, off2)
+
+
+# ----------------------------------------------------------------------------------
+# Training GEMMs: per-row scaled GEMM, token-wise quantisation, weight transpose
+# ----------------------------------------------------------------------------------
+
+def _finite_codes(rng, shape):
+    q = rng.integers(0, 256, size=shape, dtype=np.uint8)
+    q[(q & 0x7F) == 0x7F] = 0x00
+    return q
+
+
+def _dequant_rows(q, s_rows):
+    """float64 decode(q) * s for per-row-and-slice scales s [R, K/128]."""
+    dec = oracle.e4m3_decode_all()
+    return dec[q] * np.repeat(s_rows.astype(np.float64), 128, axis=1)
+
+
+def test_rowwise_gemm_reduces_to_block_gemm(oracle_lib):
+    """With the second operand's row scales equal within each 128-row block, the per-row
+    GEMM is the pinned block GEMM, bit for bit (value and bound)."""
+    rng = np.random.Generator(np.random.PCG64(11))
+    M, N, K = 37, 300, 384
+    aq, bq = _finite_codes(rng, (M, K)), _finite_codes(rng, (N, K))
+    sa = rng.uniform(0.1, 3, size=(M, K // 128)).astype(np.float32)
+    sw = rng.uniform(0.1, 3, size=(-(-N // 128), K // 128)).astype(np.float32)
+    sb = np.repeat(sw, 128, axis=0)[:N]
+    y1, b1 = oracle.block_gemm(aq, sa, bq, sw)
+    y2, b2 = oracle.rowwise_gemm(aq, sa, bq, sb)
+    assert np.array_equal(y1, y2) and np.array_equal(b1, b2)
+
+
+def test_rowwise_gemm_matches_float64_product_of_dequantised(oracle_lib):
+    """Y equals the float64 matrix product of the dequantised operands (every dequantised
+    value is exact in float64; only the summation order differs)."""
+    rng = np.random.Generator(np.random.PCG64(12))
+    M, N, K = 50, 70, 512
+    aq, bq = _finite_codes(rng, (M, K)), _finite_codes(rng, (N, K))
+    sa = rng.uniform(0.01, 2, size=(M, K // 128)).astype(np.float32)
+    sb = rng.uniform(0.01, 2, size=(N, K // 128)).astype(np.float32)
+    y, b = oracle.rowwise_gemm(aq, sa, bq, sb)
+    ref = _dequant_rows(aq, sa) @ _dequant_rows(bq, sb).T
+    assert np.all(np.abs(y - ref) <= 1e-12 * b + 1e-300)
+    ys, bs = oracle.rowwise_gemm_sampled(aq, sa, bq, sb, [0, 49, 7], [0, 69, 33])
+    assert np.array_equal(ys, y[[0, 49, 7], [0, 69, 33]]) and np.array_equal(bs, b[[0, 49, 7], [0, 69, 33]])
+
+
+def test_rowwise_gemm_row_scale_linearity(oracle_lib):
+    """Doubling the scales of one row of the second operand doubles that output column
+    exactly and leaves the others unchanged."""
+    rng = np.random.Generator(np.random.PCG64(13))
+    M, N, K = 9, 20, 256
+    aq, bq = _finite_codes(rng, (M, K)), _finite_codes(rng, (N, K))
+    sa = rng.uniform(0.1, 2, size=(M, 2)).astype(np.float32)
+    sb = rng.uniform(0.1, 2, size=(N, 2)).astype(np.float32)
+    y, _ = oracle.rowwise_gemm(aq, sa, bq, sb)
+    sb2 = sb.copy()
+    sb2[5] *= 2
+    y2, _ = oracle.rowwise_gemm(aq, sa, bq, sb2)
+    assert np.array_equal(y2[:, 5], 2 * y[:, 5])
+    assert np.array_equal(np.delete(y2, 5, axis=1), np.delete(y, 5, axis=1))
+
+
+def test_act_quant_t_closed_forms(oracle_lib):
+    """Token-wise tiles with known results: a channel whose 128 tokens all equal v has scale
+    RN_fp32(|v| / 448) and codes 0x7E / 0xFE; a zero channel has scale 0 and codes 0; in a
+    ragged last tile only the valid tokens enter the amax and the padding is code 0."""
+    M, C = 130, 16
+    x = np.zeros((M, C), dtype=np.float32)
+    vals = np.array([1.0, -3.5, 0.0078125, 1024.0, -0.5, 2.0 ** -20, 7.0, 0.0], dtype=np.float32)
+    for c in range(8):
+        x[:128, c] = vals[c]
+    x[:, 8] = 1.0
+    x[128, 8] = 6.0         # the ragged tile (tokens 128, 129) of channel 8: amax 6
+    x[129, 8] = -3.0
+    xb = synth.bf16_bits(x)
+    qt, st = oracle.act_quant_t(xb)
+    assert qt.shape == (C, 256) and st.shape == (C, 2)
+    for c in range(8):
+        v = vals[c]
+        assert st[c, 0] == np.float32(abs(v)) / np.float32(448.0)
+        want = 0 if v == 0 else (0x7E if v > 0 else 0xFE)
+        assert np.all(qt[c, :128] == want)
+    assert st[8, 1] == np.float32(6.0) / np.float32(448.0)
+    assert qt[8, 128] == 0x7E and qt[8, 129] == oracle.e4m3_encode(np.float32(-3.0) / (np.float32(6.0) / np.float32(448.0)))
+    assert np.all(qt[:, 130:] == 0)
+    assert np.all(st[9:, :] == 0) and np.all(qt[9:, :] == 0)
+
+
+def test_dgrad_through_transposed_weight_matches_dequantised_product(oracle_lib):
+    """dX = dY . W through the transposed FP8 weight equals the float64 product of the
+    dequantised dY (1x128 tiles along N) and dequantised W (128x128 blocks)."""
+    rng = np.random.Generator(np.random.PCG64(14))
+    M, N, K = 33, 256, 384
+    dy = synth.random_bf16((M, N), seed=15)
+    w = synth.random_bf16((N, K), seed=16, std=0.02)
+    dyq, sdy = oracle.act_quant(dy)
+    wq, sw = oracle.weight_quant(w)
+    wqt, swt = oracle.weight_transpose(wq, sw)
+    assert wqt.shape == (K, N) and swt.shape == (K // 128, N // 128)
+    wq2, sw2 = oracle.weight_transpose(wqt, swt)
+    assert np.array_equal(wq2, wq) and np.array_equal(sw2, sw)
+    y, b = oracle.block_gemm(dyq, sdy, wqt, swt)
+    dec = oracle.e4m3_decode_all()
+    w_deq = dec[wq] * np.repeat(np.repeat(sw.astype(np.float64), 128, axis=0), 128, axis=1)[:N]
+    ref = _dequant_rows(dyq, sdy) @ w_deq
+    assert np.all(np.abs(y - ref) <= 1e-12 * b + 1e-300)
+    del rng
