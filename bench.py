@@ -174,6 +174,75 @@ def grouped_measurement(fq, L, synth, dev, stream, steps: int, warmup: int) -> d
     }
 
 
+def backward_measurement(fq, dev, stream, steps: int, warmup: int) -> dict:
+    """Backward of the q down-projection (4096 tokens, 7168 -> 1536) through the FP8 training
+    kernels: dX = dY . W (act_quant of dY + block GEMM through the transposed weight, bf16
+    out) and dW = dY^T . X (token-wise quantisation of dY and X + per-row scaled GEMM, fp32
+    out). Inputs drawn on the device (X, dY ~ N(0, 1), W ~ N(0, 0.02)); the weight and its
+    transpose are quantised untimed. Each kernel is timed by its own event pair."""
+    import numpy as np
+    import torch
+    M, N, K = 4096, 1536, 7168
+    g = torch.Generator(device=dev).manual_seed(2)
+    x = torch.randn((M, K), generator=g, device=dev).to(torch.bfloat16)
+    dy = torch.randn((M, N), generator=g, device=dev).to(torch.bfloat16)
+    wq, sw = fq.weight_quant((torch.randn((N, K), generator=g, device=dev) * 0.02).to(torch.bfloat16))
+    wqt, swt = fq.weight_transpose(wq, sw)
+    dyq = torch.empty((M, N), dtype=torch.float8_e4m3fn, device=dev)
+    sdy = torch.empty((M, N // 128), dtype=torch.float32, device=dev)
+    dx = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    dw = torch.empty((N, K), dtype=torch.float32, device=dev)
+    ws_dx = torch.zeros(max(fq.gemm_workspace_bytes(M, K, N, torch.bfloat16), 16), dtype=torch.uint8, device=dev)
+    ws_dw = torch.zeros(max(int(fq.lib.fp8_rowwise_gemm_workspace_bytes(N, K, M, 0)), 16), dtype=torch.uint8,
+                        device=dev)
+    dyt = torch.empty((N, M), dtype=torch.float8_e4m3fn, device=dev)
+    sdyt = torch.empty((N, M // 128), dtype=torch.float32, device=dev)
+    xt = torch.empty((K, M), dtype=torch.float8_e4m3fn, device=dev)
+    sxt = torch.empty((K, M // 128), dtype=torch.float32, device=dev)
+    L = fq._lib
+    sp = stream.cuda_stream
+    calls = [
+        ("act_quant dY", lambda: fq.lib.fp8_act_quant(dy.data_ptr(), dyq.data_ptr(), sdy.data_ptr(), M, N, sp)),
+        ("dgrad GEMM", lambda: fq.lib.fp8_block_gemm(dyq.data_ptr(), sdy.data_ptr(), wqt.data_ptr(), swt.data_ptr(),
+                                                     dx.data_ptr(), L.FP8Q_OUT_BF16, M, K, N, ws_dx.data_ptr(),
+                                                     ws_dx.numel(), sp)),
+        ("act_quant_t dY", lambda: fq.lib.fp8_act_quant_t(dy.data_ptr(), dyt.data_ptr(), sdyt.data_ptr(), M, N, sp)),
+        ("act_quant_t X", lambda: fq.lib.fp8_act_quant_t(x.data_ptr(), xt.data_ptr(), sxt.data_ptr(), M, K, sp)),
+        ("wgrad GEMM", lambda: fq.lib.fp8_rowwise_gemm(dyt.data_ptr(), sdyt.data_ptr(), xt.data_ptr(), sxt.data_ptr(),
+                                                       dw.data_ptr(), L.FP8Q_OUT_F32, N, K, M, ws_dw.data_ptr(),
+                                                       ws_dw.numel(), sp)),
+    ]
+
+    def one(ev=None):
+        for i, (name, fn) in enumerate(calls):
+            if ev is not None:
+                ev[i].record(stream)
+            L.check(name, fn())
+        if ev is not None:
+            ev[len(calls)].record(stream)
+
+    for _ in range(warmup):
+        one()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        one(evs[i])
+    torch.cuda.synchronize()
+    t = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(len(calls))] for e in evs]).mean(axis=0) * 1e-3
+    total = float(t.sum())
+    gemm_flops = 2.0 * M * N * K
+    aqt_bytes = lambda R, C: R * C * 2 + R * C + C * (R // 128) * 4   # noqa: E731
+    return {
+        "workload": "q_down backward: 4096 tokens, 7168 -> 1536 (dX bf16, dW fp32 exact slices)",
+        "us": {name: round(float(v) * 1e6, 3) for (name, _), v in zip(calls, t)},
+        "total_us": round(total * 1e6, 3),
+        "tflops_incl_quant": round(2 * gemm_flops / total / 1e12, 2),
+        "dgrad_tflops": round(gemm_flops / float(t[1]) / 1e12, 2),
+        "wgrad_tflops": round(gemm_flops / float(t[4]) / 1e12, 2),
+        "act_quant_t_x_gbs": round(aqt_bytes(M, K) / float(t[3]) / 1e9, 1),
+    }
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -314,6 +383,7 @@ def main() -> int:
 
     if not args.no_extras and not args.calibrate_copy:   # (counter runs: the calibration kernel must be the only multiply)
         result["grouped_gemm"] = grouped_measurement(fq, L, synth, dev, stream, args.steps, args.warmup)
+        result["training_backward"] = backward_measurement(fq, dev, stream, min(args.steps, 50), args.warmup)
 
     if not args.no_cpu_baseline:
         cb, (oaq, osa, oy) = cpu_baseline(A_host, W_host, args.cpu_rows)
