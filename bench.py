@@ -65,8 +65,9 @@ def _per_dispatch(csv_path: str, counter: str):
             if row.get("Counter_Name") != counter:
                 continue
             name = row["Kernel_Name"]
-            # the plain GEMM (the grouped instantiation has GROUPED = 1 as its last template argument)
-            plain_gemm = "block_gemm_kernel" in name and name.split(">")[0].split(",")[-1].strip() == "0"
+            # the plain GEMM: template arguments 8 and 9 (GROUPED, ROWB) are 0
+            targs = name.split("<", 1)[1].split(">")[0].split(",") if "block_gemm_kernel<" in name else []
+            plain_gemm = len(targs) >= 9 and targs[7].strip() == "0" and targs[8].strip() == "0"
             key = ("gemm" if plain_gemm else "act_quant" if "act_quant_kernel" in name
                    else "copy" if "MulFunctor" in name else None)
             if key is None:
