@@ -55,15 +55,25 @@ def test_weight_transpose_bit_exact(N, K):
     assert np.array_equal(swt.cpu().numpy().view(np.uint32), os_.view(np.uint32))
 
 
+class RowwiseReference:
+    """The oracle's full per-row GEMM and the per-output allowances of one operand set
+    (computed once, reused across modes and configurations)."""
+
+    def __init__(self, aq, sa, bq, sb):
+        haq, hsa, hbq, hsb = host_codes(aq), sa.cpu().numpy(), host_codes(bq), sb.cpu().numpy()
+        self.y_hat, self.bound = oracle.rowwise_gemm(haq, hsa, hbq, hsb)
+        M, N = self.y_hat.shape
+        rows, cols = np.repeat(np.arange(M), N), np.tile(np.arange(N), M)
+        self.floor = scale_floor(haq, hbq, rows, cols).reshape(M, N)
+        self.fp8 = self.floor + mfma_group_allowance_rowwise(haq, hsa, hbq, hsb, rows, cols).reshape(M, N)
+
+    def check(self, y, out, mode):
+        fp8_products = mode == "fp8" or (mode == "default" and out == "bf16")
+        return gemm_check(y_host(y, out), self.y_hat, self.bound, out, self.fp8 if fp8_products else self.floor)
+
+
 def rowwise_check(aq, sa, bq, sb, y, out, mode):
-    haq, hsa, hbq, hsb = host_codes(aq), sa.cpu().numpy(), host_codes(bq), sb.cpu().numpy()
-    y_hat, bound = oracle.rowwise_gemm(haq, hsa, hbq, hsb)
-    M, N = y_hat.shape
-    rows, cols = np.repeat(np.arange(M), N), np.tile(np.arange(N), M)
-    allow = scale_floor(haq, hbq, rows, cols)
-    if mode == "fp8" or (mode == "default" and out == "bf16"):
-        allow = allow + mfma_group_allowance_rowwise(haq, hsa, hbq, hsb, rows, cols)
-    return gemm_check(y_host(y, out), y_hat, bound, out, allow.reshape(M, N))
+    return RowwiseReference(aq, sa, bq, sb).check(y, out, mode)
 
 
 @pytest.mark.parametrize("mode", ["exact", "fp8"])
@@ -92,6 +102,7 @@ def test_rowwise_every_tile_configuration(M, N, K):
     aq, sa = fq.act_quant(dev_bf16(A))
     bq, sb = fq.act_quant(dev_bf16(B))
     ws = torch.zeros(64 << 20, dtype=torch.uint8, device="cuda")
+    ref = RowwiseReference(aq, sa, bq, sb)
     names = []
     while (n := fq.lib.fp8q_gemm_config_name(len(names))) is not None:
         names.append(n.decode())
@@ -102,7 +113,7 @@ def test_rowwise_every_tile_configuration(M, N, K):
                 for out, mode in (("bf16", "fp8"), ("f32", "exact")):
                     y = fq.fp8_gemm_rowwise(aq, sa, bq, sb, out_dtype=TORCH_OUT[out], mode=mode, workspace=ws)
                     torch.cuda.synchronize()
-                    res = rowwise_check(aq, sa, bq, sb, y, out, mode)
+                    res = ref.check(y, out, mode)
                     print(f"rowwise config {name} splits {splits} {out} {mode}", res, flush=True)
                     assert res["violations"] == 0, (name, splits, out, mode, res)
     finally:
