@@ -218,6 +218,9 @@ size_t fp8_block_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int y_dty
  * of range. Process-wide and not synchronised with calls in flight on other threads.
  * fp8q_gemm_config_name(config) names a configuration ("256x256w8": BM x BN, w8 = 8
  * waves, s2 = two stages), or returns NULL past the last one. */
+/* The same choice can be made for a whole process through the environment, read once at
+ * the first GEMM call: FP8Q_GEMM_TILE=<configuration name> and FP8Q_GEMM_SPLITS=<count>.
+ * FP8Q_AQ_WGS_PER_CU=<1..32> sets fp8_act_quant's resident workgroups per CU (default 16). */
 int fp8q_gemm_force_config(int config, int splits);
 const char *fp8q_gemm_config_name(int config);
 
