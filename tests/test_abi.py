@@ -133,3 +133,51 @@ def test_python_binding_rejects_cpu_tensors_and_bad_shapes():
         fq.weight_quant(torch.zeros(4, 128, dtype=torch.bfloat16))
     with pytest.raises(ValueError):
         fq.act_quant(torch.zeros(4, 128, dtype=torch.bfloat16), block_size=64)
+
+
+def test_grouped_and_training_validation(lib):
+    """The grouped GEMM and the backward entry points reject bad arguments on the host
+    (no device is touched: every call below fails validation or is an empty no-op)."""
+    from fp8_act_quant_amd import _lib as L
+    g = lib.fp8_grouped_gemm
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 0, 4, 8, 128, None) == L.FP8Q_ERR_SHAPE       # no experts
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 1025, 4, 8, 128, None) == L.FP8Q_ERR_SHAPE    # too many
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 2, 4, 8, 100, None) == L.FP8Q_ERR_SHAPE       # K % 128
+    assert g(FAKE, FAKE, FAKE, FAKE, None, FAKE, 0, 2, 4, 8, 128, None) == L.FP8Q_ERR_NULL        # offsets
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE + 4, FAKE, 0, 2, 4, 8, 128, None) == L.FP8Q_ERR_ALIGN
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 5, 2, 4, 8, 128, None) == L.FP8Q_ERR_DTYPE
+    assert g(None, None, None, None, None, None, 0, 2, 0, 8, 128, None) == L.FP8Q_OK              # no rows
+    t = lib.fp8_act_quant_t
+    assert t(FAKE, FAKE, FAKE, 4, 12, None) == L.FP8Q_ERR_SHAPE                                    # C % 8
+    assert t(FAKE, FAKE, FAKE, -1, 16, None) == L.FP8Q_ERR_SHAPE
+    assert t(FAKE + 2, FAKE, FAKE, 4, 16, None) == L.FP8Q_ERR_ALIGN
+    assert t(FAKE, FAKE, None, 4, 16, None) == L.FP8Q_ERR_NULL
+    assert t(None, None, None, 0, 16, None) == L.FP8Q_OK
+    wt = lib.fp8_weight_transpose
+    assert wt(FAKE, FAKE, FAKE, FAKE, 16, 100, None) == L.FP8Q_ERR_SHAPE
+    assert wt(FAKE, FAKE, FAKE + 8, FAKE, 16, 128, None) == L.FP8Q_ERR_ALIGN
+    assert wt(FAKE, None, FAKE, FAKE, 16, 128, None) == L.FP8Q_ERR_NULL
+    r = lib.fp8_rowwise_gemm
+    assert r(FAKE, FAKE, FAKE, FAKE, FAKE, 9, 4, 4, 128, None, 0, None) == L.FP8Q_ERR_DTYPE
+    assert r(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 4, 4, 100, None, 0, None) == L.FP8Q_ERR_SHAPE
+    assert r(FAKE, FAKE, FAKE, FAKE, None, 0, 4, 4, 128, None, 0, None) == L.FP8Q_ERR_NULL
+    assert r(FAKE, FAKE, FAKE + 8, FAKE, FAKE, 0, 4, 4, 128, None, 0, None) == L.FP8Q_ERR_ALIGN
+    assert r(None, None, None, None, None, 0, 0, 4, 128, None, 0, None) == L.FP8Q_OK
+    assert lib.fp8_rowwise_gemm_workspace_bytes(4, 4, 100, 0) == 0
+    assert lib.fp8_rowwise_gemm_workspace_bytes(1, 1, 4096, 1) > 0      # a split-K plan for a tiny output
+
+
+def test_python_training_binding_rejects_cpu_tensors():
+    import torch
+    import fp8_act_quant_amd as fq
+    x = torch.zeros((4, 16), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fq.act_quant_t(x)                                  # not a GPU tensor
+    q = torch.zeros((4, 128), dtype=torch.float8_e4m3fn)
+    s = torch.zeros((1, 1), dtype=torch.float32)
+    with pytest.raises(ValueError):
+        fq.weight_transpose(q, s)
+    with pytest.raises(ValueError):
+        fq.fp8_gemm_rowwise(q, s, q, s)
+    with pytest.raises(ValueError):
+        fq.fp8_grouped_gemm(q, s, q.view(1, 4, 128), s.view(1, 1, 1), torch.zeros(2, dtype=torch.int64))
