@@ -39,7 +39,9 @@
 // copies and meets the other waves at the workgroup barrier, after which the next slice is
 // visible and the buffer of slice kb - 1 (now refilled during slice kb + 1) is free; then
 // it reads the next slice's first fragments while MFMAs it has already issued keep the
-// matrix unit busy.
+// matrix unit busy. Tiles whose waves have registers to spare (FP8 products, 8 waves, small
+// wave tiles) instead hold two slices' fragments in registers and read all of slice kb + 1
+// during slice kb (the `PF` schedule in the kernel).
 //
 // Split-K. For shapes with too few tiles to fill the 256 CUs the K slices are divided into
 // `splits` contiguous ranges. Each workgroup stores its fp32 partial tile to the caller's
@@ -493,11 +495,15 @@ __global__ __launch_bounds__(NW * 64) void block_gemm_kernel(GemmArgs g) {
         // stages the next slice's copies have only one slice of lead, and the barrier goes
         // after the last group's MFMAs, as late as possible (measured: 4% faster there).
         constexpr bool EARLY_BARRIER = NSTAGE >= 3;
+        // Whole-slice register prefetch (see below): FP8 products, 8 waves, and only where two
+        // register sets of a slice's fragments fit beside the accumulators.
+        constexpr bool PF = NW == 8 && !EXACT && !ROWB && SUB_M >= 2 && NSTAGE >= 3 &&
+                            (SUB_M + SUB_N) * 16 + SUB_M * SUB_N * 4 <= 160;
         // The copies queued during a slice are spread over the row groups that run before its
         // barrier (all of them with the late barrier), so that at the barrier every slice
         // queued after the next one is complete in the vector-memory count and the count
         // wait of wait_slice covers exactly the next slice.
-        constexpr int COPY_PARTS = EARLY_BARRIER ? SUB_M - 1 : SUB_M;
+        constexpr int COPY_PARTS = EARLY_BARRIER || PF ? SUB_M - 1 : SUB_M;
         static_assert(COPY_PARTS >= 1, "row groups per wave");
         const DmaPlan<BM, BN, NSTAGE, NW, ROWB * 8 + GROUPED * 4 + OUT_BF16 * 2 + EXACT, COPY_PARTS, ROWB> dma(wave, lane, g.aq, wq, g.sa, sw, m0, n0, M, N,
                                                                    K, nkb, smem + S::DUMMY);
@@ -547,157 +553,267 @@ __global__ __launch_bounds__(NW * 64) void block_gemm_kernel(GemmArgs g) {
                 return *reinterpret_cast<const float *>(base + sw_at[ONE_WS ? 0 : j]);
         };
 
-        // fragments of the slice being contracted
-        i32x8 wf[SUB_N];
-        Frag16 wh[EXACT ? SUB_N : 1];
-        WScale swv[SUB_N];
-        i32x8 af;
-        float sav;
-        auto load_slice_head = [&](const uint8_t *stage) __device__ __attribute__((always_inline)) {
+        if constexpr (PF) {
+            // Whole-slice register prefetch. Two register sets hold the fragments and scales of
+            // two slices: the MFMAs of slice kb take their operands from one set while the other
+            // is filled from LDS with slice kb + 1, so every LDS read has most of a slice of MFMA
+            // work to land behind. A stage buffer is free as soon as its slice has been read into
+            // registers, which is one slice earlier than when fragments are read as they are
+            // used, and the copies of slice kb + NSTAGE go into the buffer of slice kb.
+            // Per slice and wave: row group 0's MFMAs; the count waits for the rest of slice kb's
+            // reads and for slice kb + 1's copies, and the workgroup barrier (after which slice
+            // kb + 1 is visible and every wave has finished reading slice kb); then row groups
+            // 1 .. SUB_M - 1, whose MFMA slots also issue the reads of slice kb + 1 and the
+            // copies of slice kb + NSTAGE. Promotion runs one row group behind, as above.
+            static_assert(SUB_M >= 2, "register prefetch needs two row groups");
+            i32x8 fa[2][SUB_M], fw[2][SUB_N];
+            float sa_r[2][SUB_M];
+            WScale sw_r[2][SUB_N];
+            constexpr int NSW = ONE_WS ? 1 : SUB_N;
+            // read item `it` of a slice into register set rs: the SUB_N W fragments, then the
+            // scales, then the SUB_M A fragments (the order the slice's first row group uses them)
+            constexpr int ITEMS = SUB_N + 1 + SUB_M;
+            constexpr int SLOTS = (SUB_M - 1) * SUB_N;
+            constexpr int IPS = (ITEMS + SLOTS - 1) / SLOTS;   // read items per MFMA slot
+            auto read_item = [&](const uint8_t *stage, auto rs_c, auto it_c) __device__ __attribute__((always_inline)) {
+                constexpr int RS = decltype(rs_c)::value, IT = decltype(it_c)::value;
+                if constexpr (IT < SUB_N) {
+                    fw[RS][IT] = frag_at(stage + 16 * IT * G_SLICE, w_lo, w_hi);
+                } else if constexpr (IT == SUB_N) {
 #pragma unroll
-            for (int j = 0; j < SUB_N; ++j) wf[j] = frag_at(stage + 16 * j * G_SLICE, w_lo, w_hi);
-            af = frag_at(stage, a_lo, a_hi);
-            sav = f32_at(stage, sa_at);
+                    for (int i = 0; i < SUB_M; ++i) sa_r[RS][i] = f32_at(stage + 16 * i * 4, sa_at);
 #pragma unroll
-            for (int j = 0; j < SUB_N; ++j) swv[j] = ws_at(stage, j);
-            if constexpr (EXACT) {
+                    for (int j = 0; j < NSW; ++j) sw_r[RS][j] = ws_at(stage, j);
+                } else if constexpr (IT < ITEMS) {
+                    fa[RS][IT - SUB_N - 1] = frag_at(stage + 16 * (IT - SUB_N - 1) * G_SLICE, a_lo, a_hi);
+                }
+            };
+            f32x4 p_prev[SUB_N];
+            WScale f_prev[SUB_N];
 #pragma unroll
-                for (int j = 0; j < SUB_N; ++j) wh[j] = to_f16(wf[j]);
+            for (int j = 0; j < SUB_N; ++j) {
+                p_prev[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+                f_prev[j] = WScale{};
             }
-        };
-        load_slice_head(smem);
-
-        // promotion of each row group runs one group behind its MFMAs (the last group of a
-        // slice is promoted during the first group of the next); it starts from a zero partial
-        f32x4 p_prev[SUB_N];
-        WScale f_prev[SUB_N];
-#pragma unroll
-        for (int j = 0; j < SUB_N; ++j) {
-            p_prev[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-            f_prev[j] = WScale{};
-        }
-        // With 8 waves the K loop is unrolled by NSTAGE: each slice's stage buffer, the buffer
-        // its copies go to and the next slice's buffer are then compile-time offsets, so
-        // fragment reads use fixed addresses and the loop carries no stage index. (The 4-wave
-        // tiles hold twice the accumulators per wave; unrolled, they run out of registers, so
-        // they keep a rolled loop with a stage index.) The slice indices are wave-uniform
-        // 32-bit values, which keeps the copy and barrier conditions scalar.
-        const int kbs = __builtin_amdgcn_readfirstlane((int)kb0);
-        const int kbe = __builtin_amdgcn_readfirstlane((int)kb1);
-        // slice kb in `stage`, whose copies (slice kb + NSTAGE - 1) go to `copy_dst`, followed
-        // by the slice in `next`. A steady slice (not the first, and at least NSTAGE - 1 slices
-        // before the end) always queues copies and always has a successor: its body has no
-        // branches.
-        auto slice = [&](const uint8_t *stage, uint8_t *copy_dst, const uint8_t *next, const int kb, auto steady_c)
-                         __device__ __attribute__((always_inline)) {
-            constexpr bool STEADY = decltype(steady_c)::value;
-            const bool more = STEADY || kb + 1 < kbe;
-            const int later = STEADY ? NSTAGE - 2 : min(NSTAGE - 2, kbe - 2 - kb);
-            // the copies of slice kb + NSTAGE - 1 go into the buffer of slice kb - 1, free since
-            // the barrier that ended slice kb - 1; they are spread over this slice's row groups
-            // so that the matrix unit is never left waiting behind a burst of copy issues
-            const bool copy_now = STEADY || (kb > kbs && kb + NSTAGE - 1 < kbe);
-#pragma unroll
-            for (int i = 0; i < SUB_M; ++i) {
-                // With the early barrier, the next slice's first fragments and scales are read
-                // right after it, while this slice's last row group runs on the matrix unit:
-                // each W fragment register is refilled as soon as its last MFMA has taken it.
-                const bool head_now = EARLY_BARRIER && i == SUB_M - 1 && more;
-                i32x8 af_n = af;
-                float sav_n = sav;
-                if (head_now) {
-                    // every LDS read of slice kb is done (the last group's operands are in
-                    // registers); once all waves are past the barrier the next slice has landed
-                    wait_lgkm0();
-                    wait_slice<S::IPW, NSTAGE - 2>(later);
-                    lds_barrier();
-                    af_n = frag_at(next, a_lo, a_hi);
-                    sav_n = f32_at(next, sa_at);
-                } else if (i + 1 < SUB_M) {
-                    af_n = frag_at(stage + 16 * (i + 1) * G_SLICE, a_lo, a_hi);
-                    sav_n = f32_at(stage + 16 * (i + 1) * 4, sa_at);
-                }
-                WScale f_cur[SUB_N];
-#pragma unroll
-                for (int j = 0; j < SUB_N; ++j) f_cur[j] = sav * swv[ONE_WS ? 0 : j];
-                if (head_now) {
-#pragma unroll
-                    for (int j = 0; j < SUB_N; ++j) swv[j] = ws_at(next, j);
-                }
-                f32x4 p_cur[SUB_N];
-                const int ip = i == 0 ? SUB_M - 1 : i - 1;   // row group being promoted (a constant once unrolled)
-                if constexpr (EXACT) {
-                    const Frag16 ah = to_f16(af);
-#pragma unroll
-                    for (int j = 0; j < SUB_N; ++j) {
-                        p_cur[j] = mfma_slice_exact(wh[j], ah);
-                        if (j == 0 && copy_now && i < COPY_PARTS) dma.issue_part(copy_dst, kb + NSTAGE - 1, i);
-                        if (head_now) wf[j] = frag_at(next + 16 * j * G_SLICE, w_lo, w_hi);
-                        promote(acc[ip][j], p_prev[j], f_prev[j]);
-                        __builtin_amdgcn_sched_barrier(0);
-                    }
-                    if (head_now) {
-#pragma unroll
-                        for (int j = 0; j < SUB_N; ++j) wh[j] = to_f16(wf[j]);
-                    }
-                } else {
-#pragma unroll
-                    for (int j = 0; j < SUB_N; ++j) {
-                        p_cur[j] = mfma_slice(wf[j], af);
-                        if (j == 0 && copy_now && i < COPY_PARTS) dma.issue_part(copy_dst, kb + NSTAGE - 1, i);
-                        if (head_now) wf[j] = frag_at(next + 16 * j * G_SLICE, w_lo, w_hi);
-                        promote(acc[ip][j], p_prev[j], f_prev[j]);
-                        __builtin_amdgcn_sched_barrier(0);
-                    }
-                }
-                // with the late barrier (two stages) the next slice's first fragments load after
-                // the last group's MFMAs have taken their operands, while they run
-                if (!EARLY_BARRIER && i == SUB_M - 1 && more) {
-                    wait_slice<S::IPW, NSTAGE - 2>(later);
-                    lds_barrier();
-                    load_slice_head(next);
-                }
-#pragma unroll
-                for (int j = 0; j < SUB_N; ++j) {
-                    p_prev[j] = p_cur[j];
-                    f_prev[j] = f_cur[j];
-                }
-                if (i + 1 < SUB_M || head_now) {
-                    af = af_n;
-                    sav = sav_n;
-                }
-            }
-        };
-        const std::false_type general;
-        const std::true_type steady;
-        if constexpr (NW == 8) {
-            // slice kb uses stage (kb - kbs) % NSTAGE, a constant in each unrolled copy
+            const int kbs = __builtin_amdgcn_readfirstlane((int)kb0);
+            const int kbe = __builtin_amdgcn_readfirstlane((int)kb1);
+            // slice kb uses stage (kb - kbs) % NSTAGE and register set (kb - kbs) % 2; the loop
+            // is unrolled by a multiple of both, so each is a constant in each unrolled copy
             auto at = [&](int st) __device__ __attribute__((always_inline)) { return smem + (st % NSTAGE) * S::STAGE; };
-            slice(at(0), at(NSTAGE - 1), at(1), kbs, general);
-            int kb = kbs + 1;
-            // whole rounds of steady slices (stages 1, 2, ..., 0)
-            for (; kb + 2 * NSTAGE - 2 < kbe; kb += NSTAGE)
-                static_for<NSTAGE>([&](auto t) __device__ __attribute__((always_inline)) {
-                    constexpr int st = 1 + decltype(t)::value;
-                    slice(at(st), at(st + NSTAGE - 1), at(st + 1), kb + decltype(t)::value, steady);
-                });
-            // the last (at most 2 NSTAGE - 2) slices
-            static_for<2 * NSTAGE - 2>([&](auto t) __device__ __attribute__((always_inline)) {
-                constexpr int st = 1 + decltype(t)::value;
-                if (kb + decltype(t)::value < kbe)
-                    slice(at(st), at(st + NSTAGE - 1), at(st + 1), kb + decltype(t)::value, general);
-            });
-        } else {
-            int st = 0;
-            for (int kb = kbs; kb < kbe; ++kb) {
-                const int st_next = st + 1 == NSTAGE ? 0 : st + 1;
-                const int st_copy = st == 0 ? NSTAGE - 1 : st - 1;
-                slice(smem + st * S::STAGE, smem + st_copy * S::STAGE, smem + st_next * S::STAGE, kb, general);
-                st = st_next;
-            }
-        }
+            const std::integral_constant<int, 0> set0;
+            static_for<ITEMS>([&](auto it) __device__ __attribute__((always_inline)) { read_item(at(0), set0, it); });
+            auto step = [&](auto t_c, const int kb, auto steady_c) __device__ __attribute__((always_inline)) {
+                constexpr int T = decltype(t_c)::value;
+                constexpr bool STEADY = decltype(steady_c)::value;
+                constexpr int R = T & 1;
+                const std::integral_constant<int, R ^ 1> set_next;
+                const bool more = STEADY || kb + 1 < kbe;
+                const bool copy_now = STEADY || kb + NSTAGE < kbe;
+                const int later = STEADY ? NSTAGE - 2 : min(NSTAGE - 2, kbe - 2 - kb);
+                const uint8_t *next = at(T + 1);
+                uint8_t *copy_dst = at(T);
+                // (the compiler waits for each register of set R as its first MFMA needs it)
+                static_for<SUB_M>([&](auto i_c) __device__ __attribute__((always_inline)) {
+                    constexpr int I = decltype(i_c)::value;
+                    constexpr int IP = I == 0 ? SUB_M - 1 : I - 1;   // row group being promoted
+                    WScale f_cur[SUB_N];
 #pragma unroll
-        for (int j = 0; j < SUB_N; ++j) promote(acc[SUB_M - 1][j], p_prev[j], f_prev[j]);
+                    for (int j = 0; j < SUB_N; ++j) f_cur[j] = sa_r[R][I] * sw_r[R][ONE_WS ? 0 : j];
+                    f32x4 p_cur[SUB_N];
+                    static_for<SUB_N>([&](auto j_c) __device__ __attribute__((always_inline)) {
+                        constexpr int J = decltype(j_c)::value;
+                        p_cur[J] = mfma_slice(fw[R][J], fa[R][I]);
+                        if constexpr (I >= 1) {
+                            if (J == 0 && copy_now) dma.issue_part(copy_dst, kb + NSTAGE, I - 1);
+                            if (more)
+                                static_for<IPS>([&](auto u_c) __device__ __attribute__((always_inline)) {
+                                    read_item(next, set_next,
+                                              std::integral_constant<int, ((I - 1) * SUB_N + J) * IPS + decltype(u_c)::value>{});
+                                });
+                        }
+                        promote(acc[IP][J], p_prev[J], f_prev[J]);
+                        __builtin_amdgcn_sched_barrier(0);
+                    });
+#pragma unroll
+                    for (int j = 0; j < SUB_N; ++j) {
+                        p_prev[j] = p_cur[j];
+                        f_prev[j] = f_cur[j];
+                    }
+                    if constexpr (I == 0) {
+                        if (more) {
+                            // every read of slice kb has landed before the barrier that frees its buffer
+                            wait_lgkm0();
+                            wait_slice<S::IPW, NSTAGE - 2>(later);
+                            lds_barrier();
+                        }
+                    }
+                });
+            };
+            const std::false_type general;
+            const std::true_type steady;
+            constexpr int U = NSTAGE % 2 == 0 ? NSTAGE : 2 * NSTAGE;
+            int kb = kbs;
+            for (; kb + U - 1 + NSTAGE < kbe; kb += U)
+                static_for<U>([&](auto t) __device__ __attribute__((always_inline)) { step(t, kb + decltype(t)::value, steady); });
+            // the last (at most U - 1 + NSTAGE) slices
+            static_for<U - 1 + NSTAGE>([&](auto t) __device__ __attribute__((always_inline)) {
+                if (kb + decltype(t)::value < kbe) step(t, kb + decltype(t)::value, general);
+            });
+#pragma unroll
+            for (int j = 0; j < SUB_N; ++j) promote(acc[SUB_M - 1][j], p_prev[j], f_prev[j]);
+        } else {
+            // fragments of the slice being contracted
+            i32x8 wf[SUB_N];
+            Frag16 wh[EXACT ? SUB_N : 1];
+            WScale swv[SUB_N];
+            i32x8 af;
+            float sav;
+            auto load_slice_head = [&](const uint8_t *stage) __device__ __attribute__((always_inline)) {
+    #pragma unroll
+                for (int j = 0; j < SUB_N; ++j) wf[j] = frag_at(stage + 16 * j * G_SLICE, w_lo, w_hi);
+                af = frag_at(stage, a_lo, a_hi);
+                sav = f32_at(stage, sa_at);
+    #pragma unroll
+                for (int j = 0; j < SUB_N; ++j) swv[j] = ws_at(stage, j);
+                if constexpr (EXACT) {
+    #pragma unroll
+                    for (int j = 0; j < SUB_N; ++j) wh[j] = to_f16(wf[j]);
+                }
+            };
+            load_slice_head(smem);
+
+            // promotion of each row group runs one group behind its MFMAs (the last group of a
+            // slice is promoted during the first group of the next); it starts from a zero partial
+            f32x4 p_prev[SUB_N];
+            WScale f_prev[SUB_N];
+    #pragma unroll
+            for (int j = 0; j < SUB_N; ++j) {
+                p_prev[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+                f_prev[j] = WScale{};
+            }
+            // With 8 waves the K loop is unrolled by NSTAGE: each slice's stage buffer, the buffer
+            // its copies go to and the next slice's buffer are then compile-time offsets, so
+            // fragment reads use fixed addresses and the loop carries no stage index. (The 4-wave
+            // tiles hold twice the accumulators per wave; unrolled, they run out of registers, so
+            // they keep a rolled loop with a stage index.) The slice indices are wave-uniform
+            // 32-bit values, which keeps the copy and barrier conditions scalar.
+            const int kbs = __builtin_amdgcn_readfirstlane((int)kb0);
+            const int kbe = __builtin_amdgcn_readfirstlane((int)kb1);
+            // slice kb in `stage`, whose copies (slice kb + NSTAGE - 1) go to `copy_dst`, followed
+            // by the slice in `next`. A steady slice (not the first, and at least NSTAGE - 1 slices
+            // before the end) always queues copies and always has a successor: its body has no
+            // branches.
+            auto slice = [&](const uint8_t *stage, uint8_t *copy_dst, const uint8_t *next, const int kb, auto steady_c)
+                             __device__ __attribute__((always_inline)) {
+                constexpr bool STEADY = decltype(steady_c)::value;
+                const bool more = STEADY || kb + 1 < kbe;
+                const int later = STEADY ? NSTAGE - 2 : min(NSTAGE - 2, kbe - 2 - kb);
+                // the copies of slice kb + NSTAGE - 1 go into the buffer of slice kb - 1, free since
+                // the barrier that ended slice kb - 1; they are spread over this slice's row groups
+                // so that the matrix unit is never left waiting behind a burst of copy issues
+                const bool copy_now = STEADY || (kb > kbs && kb + NSTAGE - 1 < kbe);
+    #pragma unroll
+                for (int i = 0; i < SUB_M; ++i) {
+                    // With the early barrier, the next slice's first fragments and scales are read
+                    // right after it, while this slice's last row group runs on the matrix unit:
+                    // each W fragment register is refilled as soon as its last MFMA has taken it.
+                    const bool head_now = EARLY_BARRIER && i == SUB_M - 1 && more;
+                    i32x8 af_n = af;
+                    float sav_n = sav;
+                    if (head_now) {
+                        // every LDS read of slice kb is done (the last group's operands are in
+                        // registers); once all waves are past the barrier the next slice has landed
+                        wait_lgkm0();
+                        wait_slice<S::IPW, NSTAGE - 2>(later);
+                        lds_barrier();
+                        af_n = frag_at(next, a_lo, a_hi);
+                        sav_n = f32_at(next, sa_at);
+                    } else if (i + 1 < SUB_M) {
+                        af_n = frag_at(stage + 16 * (i + 1) * G_SLICE, a_lo, a_hi);
+                        sav_n = f32_at(stage + 16 * (i + 1) * 4, sa_at);
+                    }
+                    WScale f_cur[SUB_N];
+    #pragma unroll
+                    for (int j = 0; j < SUB_N; ++j) f_cur[j] = sav * swv[ONE_WS ? 0 : j];
+                    if (head_now) {
+    #pragma unroll
+                        for (int j = 0; j < SUB_N; ++j) swv[j] = ws_at(next, j);
+                    }
+                    f32x4 p_cur[SUB_N];
+                    const int ip = i == 0 ? SUB_M - 1 : i - 1;   // row group being promoted (a constant once unrolled)
+                    if constexpr (EXACT) {
+                        const Frag16 ah = to_f16(af);
+    #pragma unroll
+                        for (int j = 0; j < SUB_N; ++j) {
+                            p_cur[j] = mfma_slice_exact(wh[j], ah);
+                            if (j == 0 && copy_now && i < COPY_PARTS) dma.issue_part(copy_dst, kb + NSTAGE - 1, i);
+                            if (head_now) wf[j] = frag_at(next + 16 * j * G_SLICE, w_lo, w_hi);
+                            promote(acc[ip][j], p_prev[j], f_prev[j]);
+                            __builtin_amdgcn_sched_barrier(0);
+                        }
+                        if (head_now) {
+    #pragma unroll
+                            for (int j = 0; j < SUB_N; ++j) wh[j] = to_f16(wf[j]);
+                        }
+                    } else {
+    #pragma unroll
+                        for (int j = 0; j < SUB_N; ++j) {
+                            p_cur[j] = mfma_slice(wf[j], af);
+                            if (j == 0 && copy_now && i < COPY_PARTS) dma.issue_part(copy_dst, kb + NSTAGE - 1, i);
+                            if (head_now) wf[j] = frag_at(next + 16 * j * G_SLICE, w_lo, w_hi);
+                            promote(acc[ip][j], p_prev[j], f_prev[j]);
+                            __builtin_amdgcn_sched_barrier(0);
+                        }
+                    }
+                    // with the late barrier (two stages) the next slice's first fragments load after
+                    // the last group's MFMAs have taken their operands, while they run
+                    if (!EARLY_BARRIER && i == SUB_M - 1 && more) {
+                        wait_slice<S::IPW, NSTAGE - 2>(later);
+                        lds_barrier();
+                        load_slice_head(next);
+                    }
+    #pragma unroll
+                    for (int j = 0; j < SUB_N; ++j) {
+                        p_prev[j] = p_cur[j];
+                        f_prev[j] = f_cur[j];
+                    }
+                    if (i + 1 < SUB_M || head_now) {
+                        af = af_n;
+                        sav = sav_n;
+                    }
+                }
+            };
+            const std::false_type general;
+            const std::true_type steady;
+            if constexpr (NW == 8) {
+                // slice kb uses stage (kb - kbs) % NSTAGE, a constant in each unrolled copy
+                auto at = [&](int st) __device__ __attribute__((always_inline)) { return smem + (st % NSTAGE) * S::STAGE; };
+                slice(at(0), at(NSTAGE - 1), at(1), kbs, general);
+                int kb = kbs + 1;
+                // whole rounds of steady slices (stages 1, 2, ..., 0)
+                for (; kb + 2 * NSTAGE - 2 < kbe; kb += NSTAGE)
+                    static_for<NSTAGE>([&](auto t) __device__ __attribute__((always_inline)) {
+                        constexpr int st = 1 + decltype(t)::value;
+                        slice(at(st), at(st + NSTAGE - 1), at(st + 1), kb + decltype(t)::value, steady);
+                    });
+                // the last (at most 2 NSTAGE - 2) slices
+                static_for<2 * NSTAGE - 2>([&](auto t) __device__ __attribute__((always_inline)) {
+                    constexpr int st = 1 + decltype(t)::value;
+                    if (kb + decltype(t)::value < kbe)
+                        slice(at(st), at(st + NSTAGE - 1), at(st + 1), kb + decltype(t)::value, general);
+                });
+            } else {
+                int st = 0;
+                for (int kb = kbs; kb < kbe; ++kb) {
+                    const int st_next = st + 1 == NSTAGE ? 0 : st + 1;
+                    const int st_copy = st == 0 ? NSTAGE - 1 : st - 1;
+                    slice(smem + st * S::STAGE, smem + st_copy * S::STAGE, smem + st_next * S::STAGE, kb, general);
+                    st = st_next;
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < SUB_N; ++j) promote(acc[SUB_M - 1][j], p_prev[j], f_prev[j]);
+        }
     }
 
     if (g.splits > 1) {
