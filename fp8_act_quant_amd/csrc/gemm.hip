@@ -503,7 +503,7 @@ __global__ __launch_bounds__(NW * 64) void block_gemm_kernel(GemmArgs g) {
         // barrier (all of them with the late barrier), so that at the barrier every slice
         // queued after the next one is complete in the vector-memory count and the count
         // wait of wait_slice covers exactly the next slice.
-        constexpr int COPY_PARTS = EARLY_BARRIER || PF ? SUB_M - 1 : SUB_M;
+        constexpr int COPY_PARTS = PF ? (SUB_M - 1) * SUB_N : EARLY_BARRIER ? SUB_M - 1 : SUB_M;
         static_assert(COPY_PARTS >= 1, "row groups per wave");
         const DmaPlan<BM, BN, NSTAGE, NW, ROWB * 8 + GROUPED * 4 + OUT_BF16 * 2 + EXACT, COPY_PARTS, ROWB> dma(wave, lane, g.aq, wq, g.sa, sw, m0, n0, M, N,
                                                                    K, nkb, smem + S::DUMMY);
@@ -624,7 +624,9 @@ __global__ __launch_bounds__(NW * 64) void block_gemm_kernel(GemmArgs g) {
                         constexpr int J = decltype(j_c)::value;
                         p_cur[J] = mfma_slice(fw[R][J], fa[R][I]);
                         if constexpr (I >= 1) {
-                            if (J == 0 && copy_now) dma.issue_part(copy_dst, kb + NSTAGE, I - 1);
+                            // one copy instruction per MFMA slot: a wave whose copy waits for the
+                            // address unit stalls its in-order issue, MFMAs included
+                            if (copy_now) dma.issue_part(copy_dst, kb + NSTAGE, (I - 1) * SUB_N + J);
                             if (more)
                                 static_for<IPS>([&](auto u_c) __device__ __attribute__((always_inline)) {
                                     read_item(next, set_next,
