@@ -503,8 +503,11 @@ __global__ __launch_bounds__(NW * 64) void block_gemm_kernel(GemmArgs g) {
         // barrier (all of them with the late barrier), so that at the barrier every slice
         // queued after the next one is complete in the vector-memory count and the count
         // wait of wait_slice covers exactly the next slice.
-        constexpr int COPY_PARTS = PF ? (SUB_M - 1) * SUB_N : EARLY_BARRIER ? SUB_M - 1 : SUB_M;
-        static_assert(COPY_PARTS >= 1, "row groups per wave");
+        // Each MFMA slot of those row groups issues at most one copy instruction: a wave whose
+        // copy waits for the address unit stalls its in-order issue, MFMAs included.
+        constexpr int COPY_GROUPS = EARLY_BARRIER || PF ? SUB_M - 1 : SUB_M;
+        static_assert(COPY_GROUPS >= 1, "row groups per wave");
+        constexpr int COPY_PARTS = COPY_GROUPS * SUB_N;
         const DmaPlan<BM, BN, NSTAGE, NW, ROWB * 8 + GROUPED * 4 + OUT_BF16 * 2 + EXACT, COPY_PARTS, ROWB> dma(wave, lane, g.aq, wq, g.sa, sw, m0, n0, M, N,
                                                                    K, nkb, smem + S::DUMMY);
         // prologue: the first NSTAGE slices in flight
@@ -624,8 +627,6 @@ __global__ __launch_bounds__(NW * 64) void block_gemm_kernel(GemmArgs g) {
                         constexpr int J = decltype(j_c)::value;
                         p_cur[J] = mfma_slice(fw[R][J], fa[R][I]);
                         if constexpr (I >= 1) {
-                            // one copy instruction per MFMA slot: a wave whose copy waits for the
-                            // address unit stalls its in-order issue, MFMAs included
                             if (copy_now) dma.issue_part(copy_dst, kb + NSTAGE, (I - 1) * SUB_N + J);
                             if (more)
                                 static_for<IPS>([&](auto u_c) __device__ __attribute__((always_inline)) {
@@ -748,7 +749,7 @@ __global__ __launch_bounds__(NW * 64) void block_gemm_kernel(GemmArgs g) {
     #pragma unroll
                         for (int j = 0; j < SUB_N; ++j) {
                             p_cur[j] = mfma_slice_exact(wh[j], ah);
-                            if (j == 0 && copy_now && i < COPY_PARTS) dma.issue_part(copy_dst, kb + NSTAGE - 1, i);
+                            if (copy_now && i < COPY_GROUPS) dma.issue_part(copy_dst, kb + NSTAGE - 1, i * SUB_N + j);
                             if (head_now) wf[j] = frag_at(next + 16 * j * G_SLICE, w_lo, w_hi);
                             promote(acc[ip][j], p_prev[j], f_prev[j]);
                             __builtin_amdgcn_sched_barrier(0);
@@ -761,7 +762,7 @@ __global__ __launch_bounds__(NW * 64) void block_gemm_kernel(GemmArgs g) {
     #pragma unroll
                         for (int j = 0; j < SUB_N; ++j) {
                             p_cur[j] = mfma_slice(wf[j], af);
-                            if (j == 0 && copy_now && i < COPY_PARTS) dma.issue_part(copy_dst, kb + NSTAGE - 1, i);
+                            if (copy_now && i < COPY_GROUPS) dma.issue_part(copy_dst, kb + NSTAGE - 1, i * SUB_N + j);
                             if (head_now) wf[j] = frag_at(next + 16 * j * G_SLICE, w_lo, w_hi);
                             promote(acc[ip][j], p_prev[j], f_prev[j]);
                             __builtin_amdgcn_sched_barrier(0);
