@@ -498,7 +498,7 @@ __global__ __launch_bounds__(NW * 64) void block_gemm_kernel(GemmArgs g) {
         // Whole-slice register prefetch (see below): FP8 products, 8 waves, and only where two
         // register sets of a slice's fragments fit beside the accumulators.
         constexpr bool PF = NW == 8 && !EXACT && !ROWB && SUB_M >= 2 && NSTAGE >= 3 &&
-                            (SUB_M + SUB_N) * 16 + SUB_M * SUB_N * 4 <= 160;
+                            (SUB_M + SUB_N) * 16 + SUB_M * SUB_N * 4 <= 192;
         // The copies queued during a slice are spread over the row groups that run before its
         // barrier (all of them with the late barrier), so that at the barrier every slice
         // queued after the next one is complete in the vector-memory count and the count
