@@ -298,6 +298,35 @@ def test_gemm_every_tile_configuration(M, N, K):
         fq.lib.fp8q_gemm_force_config(-1, 0)
 
 
+@pytest.mark.parametrize("nkb", [1, 2, 3, 4, 5, 6, 7, 8, 9, 14, 15])
+def test_gemm_every_tile_every_slice_count(nkb):
+    """Every tile configuration at every short slice count: the K loops are unrolled by
+    their stage count (and, with the register prefetch, by twice that) and end in a
+    remainder of up to that many slices plus the pipeline depth, so each count from 1 to 9
+    (and 14, 15) takes a different path through the remainder. FP8 products and bf16 out
+    (the register-prefetch schedule's mode) and fp32 exact slices, one split."""
+    from fp8_act_quant_amd import _lib as L
+    M, N, K = 260, 200, 128 * nkb
+    A = synth.random_bf16((M, K), seed=7919 + nkb)
+    W = synth.random_bf16((N, K), seed=104729 + nkb, std=0.02)
+    aq, sa, wq, sw = quantise_on_gpu(A, W)
+    haq, hsa, hwq, hsw = host_codes(aq), sa.cpu().numpy(), host_codes(wq), sw.cpu().numpy()
+    y_hat, bound = oracle.block_gemm(haq, hsa, hwq, hsw)
+    rows, cols = np.repeat(np.arange(M), N), np.tile(np.arange(N), M)
+    floor = scale_floor(haq, hwq, rows, cols).reshape(M, N)
+    fp8_allow = floor + mfma_group_allowance(haq, hsa, hwq, hsw, rows, cols).reshape(M, N)
+    try:
+        for c, name in enumerate(_configs()):
+            assert fq.lib.fp8q_gemm_force_config(c, 1) == L.FP8Q_OK
+            for out, mode in (("bf16", "fp8"), ("f32", "exact")):
+                y = fq.fp8_gemm(aq, sa, wq, sw, out_dtype=TORCH_OUT[out], mode=mode)
+                torch.cuda.synchronize()
+                res = gemm_check(y_host(y, out), y_hat, bound, out, fp8_allow if mode == "fp8" else floor)
+                assert res["violations"] == 0, (name, nkb, out, mode, res)
+    finally:
+        fq.lib.fp8q_gemm_force_config(-1, 0)
+
+
 def test_linear_dispatch():
     """linear(): the FP8 branch is act_quant + fp8_gemm with the bias fused; the bf16
     branch dequantises the weight and applies torch's linear; a bf16 weight is used as is."""
