@@ -11,7 +11,6 @@ stream. Every arithmetic step runs in the gfx950 kernels behind that library.
 """
 from __future__ import annotations
 
-import ctypes
 import math
 
 import torch
@@ -193,55 +192,6 @@ def fp8_gemm(a: torch.Tensor, a_s: torch.Tensor, w: torch.Tensor, w_s: torch.Ten
                                                              w_s.data_ptr(), b_ptr, out.data_ptr(), code, M, N, K,
                                                              ws_ptr or None, ws_bytes, _stream(a)))
     return out
-
-
-def act_quant_gemm(x: torch.Tensor, w: torch.Tensor, w_s: torch.Tensor, out_dtype=torch.bfloat16,
-                   workspace="auto", mode: str = "default", return_path: bool = False):
-    """act_quant(x) followed by fp8_gemm in one library call (fp8_act_quant_gemm).
-
-    x: bfloat16 [..., K]; w: float8_e4m3fn [N, K] with scales [ceil(N/128), K/128].
-    Returns ``(y, q, s)``: y [..., N] in out_dtype and the quantised activations (q, s), the
-    same values act_quant(x) and fp8_gemm(q, s, w, w_s) give. With return_path=True a fourth
-    value tells whether the one-launch fused path ran. workspace as for fp8_gemm ("auto": a
-    zeroed workspace cached per device and stream); without one the two kernels run."""
-    if mode not in _MODES:
-        raise ValueError(f"mode must be one of {sorted(_MODES)}")
-    _need(x, "x", torch.bfloat16)
-    _need(w, "w", torch.float8_e4m3fn)
-    _need(w_s, "w_s", torch.float32, align=4)
-    if out_dtype not in (torch.float32, torch.bfloat16):
-        raise TypeError("out_dtype must be torch.float32 or torch.bfloat16")
-    K = x.shape[-1]
-    if w.dim() != 2 or w.shape[1] != K:
-        raise ValueError("w must be [N, K] with the activation's K")
-    if K % BLOCK:
-        raise ValueError("K must be a multiple of 128")
-    N = w.shape[0]
-    M = math.prod(x.shape[:-1])
-    if tuple(w_s.shape) != ((N + BLOCK - 1) // BLOCK, K // BLOCK):
-        raise ValueError("w_s must be [ceil(N/128), K/128]")
-    q = torch.empty(x.shape, dtype=torch.float8_e4m3fn, device=x.device)
-    s = torch.empty((*x.shape[:-1], K // BLOCK), dtype=torch.float32, device=x.device)
-    y = torch.empty((*x.shape[:-1], N), dtype=out_dtype, device=x.device)
-    code = _gemm_code(out_dtype, mode)
-    ws_ptr, ws_bytes = 0, 0
-    if isinstance(workspace, str):
-        if workspace != "auto":
-            raise ValueError('workspace must be "auto", None or a tensor')
-        need = int(lib.fp8_act_quant_gemm_workspace_bytes(M, N, K, code)) if M and N and K else 0
-        if need:
-            ws = _auto_workspace(x.device, _stream(x), need)
-            ws_ptr, ws_bytes = ws.data_ptr(), ws.numel()
-    elif workspace is not None:
-        _need(workspace, "workspace", workspace.dtype)
-        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
-    fused = ctypes.c_int(0)
-    with torch.cuda.device(x.device):
-        check("fp8_act_quant_gemm", lib.fp8_act_quant_gemm(x.data_ptr(), q.data_ptr(), s.data_ptr(), w.data_ptr(),
-                                                           w_s.data_ptr(), y.data_ptr(), code, M, N, K,
-                                                           ws_ptr or None, ws_bytes, ctypes.byref(fused),
-                                                           _stream(x)))
-    return (y, q, s, bool(fused.value)) if return_path else (y, q, s)
 
 
 def fp8_grouped_gemm(a: torch.Tensor, a_s: torch.Tensor, w: torch.Tensor, w_s: torch.Tensor,

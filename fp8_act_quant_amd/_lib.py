@@ -37,9 +37,6 @@ SIGNATURES = {
     "fp8_block_gemm_bias": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.c_int, _I64, _I64, _I64, _P,
                                            ctypes.c_size_t, _P]),
     "fp8_block_gemm_workspace_bytes": (ctypes.c_size_t, [_I64, _I64, _I64, ctypes.c_int]),
-    "fp8_act_quant_gemm": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.c_int, _I64, _I64, _I64, _P,
-                                          ctypes.c_size_t, ctypes.POINTER(ctypes.c_int), _P]),
-    "fp8_act_quant_gemm_workspace_bytes": (ctypes.c_size_t, [_I64, _I64, _I64, ctypes.c_int]),
     "fp8_grouped_gemm": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.c_int, _I64, _I64, _I64, _I64, _P]),
     "fp8_act_quant_t": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _P]),
     "fp8_weight_transpose": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _P]),

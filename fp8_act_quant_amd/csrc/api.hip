@@ -113,50 +113,6 @@ int fp8_block_gemm_bias(const uint8_t *aq, const float *sa, const uint8_t *wq, c
                                           workspace, workspace_bytes, static_cast<hipStream_t>(stream)));
 }
 
-int fp8_act_quant_gemm(const uint16_t *x, uint8_t *aq, float *sa, const uint8_t *wq, const float *sw, void *y,
-                       int y_dtype, int64_t M, int64_t N, int64_t K, void *workspace, size_t workspace_bytes,
-                       int *fused, void *stream) {
-    if (fused) *fused = 0;
-    const int dtype = y_dtype & 0xFF;
-    const int mode = y_dtype & ~0xFF;
-    if (dtype != FP8Q_OUT_F32 && dtype != FP8Q_OUT_BF16) return FP8Q_ERR_DTYPE;
-    if (mode != 0 && mode != FP8Q_GEMM_FP8_PRODUCTS && mode != FP8Q_GEMM_EXACT_SLICES) return FP8Q_ERR_DTYPE;
-    if (int e = shape_ok(M, K)) return e;
-    if (int e = shape_ok(N, K)) return e;
-    if (M > 0 && N > kMaxElems / M) return FP8Q_ERR_SHAPE;
-    if (K > kMaxGemmK) return FP8Q_ERR_SHAPE;
-    if (M == 0) return FP8Q_OK;
-    if (!y && N > 0) return FP8Q_ERR_NULL;
-    if (K > 0 && (!x || !aq || !sa || (N > 0 && (!wq || !sw)))) return FP8Q_ERR_NULL;
-    if (misaligned(x, 16) || misaligned(aq, 16) || misaligned(wq, 16) || misaligned(y, 16) || misaligned(sa, 4) ||
-        misaligned(sw, 4))
-        return FP8Q_ERR_ALIGN;
-    if (workspace == nullptr) workspace_bytes = 0;
-    if (workspace_bytes && misaligned(workspace, 16)) return FP8Q_ERR_ALIGN;
-    if (int e = check_device()) return e;
-    const bool exact = mode == FP8Q_GEMM_EXACT_SLICES || (mode == 0 && dtype == FP8Q_OUT_F32);
-    if (K == 0) {   // no activations to quantise; the GEMM writes zeros
-        if (N == 0) return FP8Q_OK;
-        return finish(fp8q::launch_block_gemm(aq, sa, wq, sw, nullptr, y, dtype == FP8Q_OUT_BF16, exact, M, N, K,
-                                              workspace, workspace_bytes, static_cast<hipStream_t>(stream)));
-    }
-    if (N == 0)
-        return finish(fp8q::launch_act_quant(x, aq, sa, M, K, static_cast<hipStream_t>(stream)));
-    return finish(fp8q::launch_act_quant_gemm(x, aq, sa, wq, sw, y, dtype == FP8Q_OUT_BF16, exact, M, N, K, workspace,
-                                              workspace_bytes, static_cast<hipStream_t>(stream), fused));
-}
-
-size_t fp8_act_quant_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int y_dtype) {
-    if (M <= 0 || N <= 0 || K <= 0 || (K % kBlock) != 0 || K > kMaxGemmK) return 0;
-    if (N > kMaxElems / M || shape_ok(M, K) || shape_ok(N, K)) return 0;
-    const int dtype = y_dtype & 0xFF;
-    const int mode = y_dtype & ~0xFF;
-    if (dtype != FP8Q_OUT_F32 && dtype != FP8Q_OUT_BF16) return 0;
-    if (mode != 0 && mode != FP8Q_GEMM_FP8_PRODUCTS && mode != FP8Q_GEMM_EXACT_SLICES) return 0;
-    const bool exact = mode == FP8Q_GEMM_EXACT_SLICES || (mode == 0 && dtype == FP8Q_OUT_F32);
-    return fp8q::act_quant_gemm_workspace_bytes(M, N, K, dtype == FP8Q_OUT_BF16, exact);
-}
-
 int fp8_grouped_gemm(const uint8_t *aq, const float *sa, const uint8_t *wq, const float *sw, const int64_t *offsets,
                      void *y, int y_dtype, int64_t experts, int64_t rows, int64_t N, int64_t K, void *stream) {
     const int dtype = y_dtype & 0xFF;
@@ -268,6 +224,6 @@ const char *fp8q_strerror(int status) {
     }
 }
 
-int fp8q_version(void) { return (1 << 16) | 3; }
+int fp8q_version(void) { return (1 << 16) | 2; }
 
 }  // extern "C"

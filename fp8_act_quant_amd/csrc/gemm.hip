@@ -81,10 +81,8 @@ __device__ __forceinline__ void static_for(F &&f) {
 }
 
 // ROWB: the second operand has one scale per row and slice (sw [N, K/128], the layout of
-// the activation scales) instead of one per 128-row block and slice. FUSED (act_quant in the
-// GEMM): per-wave landing slots of the arrival-count polls (256 B each) and two buffers that
-// stage the activation chunks a wave quantises (1 KiB per wave each).
-template <int BM, int BN, int NSTAGE, int NW, int ROWB = 0, int FUSED = 0>
+// the activation scales) instead of one per 128-row block and slice.
+template <int BM, int BN, int NSTAGE, int NW, int ROWB = 0>
 struct GemmSmem {
     static_assert(BM % 64 == 0 && BN % 64 == 0 && BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "tile shape");
     static constexpr int A_BYTES = BM * G_SLICE;
@@ -94,10 +92,8 @@ struct GemmSmem {
     static constexpr int SW_BYTES = ROWB ? BN * 4 : 64 * 4;
     static constexpr int STAGE = A_BYTES + W_BYTES + SA_BYTES + SW_BYTES;
     static constexpr int DUMMY = STAGE * NSTAGE;   // 256-byte landing area of padding copies
-    static constexpr int FLAG = DUMMY + 256;       // split-K / fused "last to arrive" flag
-    static constexpr int POLL = FLAG + 16;
-    static constexpr int XSTAGE = POLL + (FUSED ? NW * 256 : 0);
-    static constexpr int TOTAL = XSTAGE + (FUSED ? 2 * NW * 1024 : 0);
+    static constexpr int FLAG = DUMMY + 256;       // split-K "last to arrive" flag
+    static constexpr int TOTAL = FLAG + 16;
     // LDS-DMA instructions per wave and slice: each tile instruction moves 1 KiB (8 rows of
     // 128 B), each scale instruction 256 B (64 rows of one fp32)
     static constexpr int A_INSTR = BM / (8 * NW), W_INSTR = BN / (8 * NW);
@@ -229,11 +225,9 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *p, int64_t bytes) {
 // the activation-scale instructions.
 // VARIANT makes the type unique to each kernel instantiation: when kernels of different
 // variants shared one DmaPlan type, the host compiler emitted a launch stub for only one of them.
-// ACACHE: cache policy of the activation tile and scale copies (device scope where another
-// workgroup of the same launch has just written them).
-template <int BM, int BN, int NSTAGE, int NW, int VARIANT, int NG, int ROWB, int ACACHE = 0, int FUSED = 0>
+template <int BM, int BN, int NSTAGE, int NW, int VARIANT, int NG, int ROWB>
 struct DmaPlan {
-    using S = GemmSmem<BM, BN, NSTAGE, NW, ROWB, FUSED>;
+    using S = GemmSmem<BM, BN, NSTAGE, NW, ROWB>;
     rsrc_t ra, rw, rsa, rsw;
     uint32_t off[S::IPW];
     int w;
@@ -287,7 +281,7 @@ struct DmaPlan {
     __device__ __forceinline__ void issue_one(uint8_t *base, int koff, int soff, int I) const {
         if (I < S::A_INSTR) {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(base + 8 * (NW * I + w) * G_SLICE), 16, off[I],
-                                                     koff, 0, ACACHE);
+                                                     koff, 0, 0);
         } else if (I < S::A_INSTR + S::W_INSTR) {
             const int t = I - S::A_INSTR;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void *)(base + S::A_BYTES + 8 * (NW * t + w) * G_SLICE),
@@ -295,7 +289,7 @@ struct DmaPlan {
         } else if (I < S::IPW - S::SW_INSTR) {
             const int b = NW * (I - S::A_INSTR - S::W_INSTR) + w;
             uint8_t *dst = b < S::SA_BLOCKS ? base + S::A_BYTES + S::W_BYTES + b * 256 : dummy;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_void *)dst, 4, off[I], soff, 0, ACACHE);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_void *)dst, 4, off[I], soff, 0, 0);
         } else if (ROWB) {
             const int b = NW * (I - (S::IPW - S::SW_INSTR)) + w;
             uint8_t *dst = b < S::SB_BLOCKS ? base + S::A_BYTES + S::W_BYTES + S::SA_BYTES + b * 256 : dummy;
@@ -344,119 +338,9 @@ struct GemmArgs {
     int64_t M, N, K;
     int tiles_m, tiles_n, group, splits;
     int experts;
-    // fused act_quant: the bf16 activations (aq and sa are then written by the kernel) and
-    // the arrival counters (see FusedQuant); null otherwise
-    const uint16_t *x;
-    uint32_t *sync;
 };
 
 constexpr int kMaxExperts = (int)kMaxGroupedExperts;
-
-// ---------------------------------------------------------------------------------------
-// Fused act_quant (the FUSED kernel: one workgroup per output tile, all of them resident at
-// once). The tiles_n workgroups of a row band (the tiles that share BM rows of A) quantise
-// those rows slice by slice ahead of the contraction. Workgroup j of the band takes rows
-// [j RP, (j+1) RP) of it, RP = ceil(BM / tiles_n) <= 32, with act_quant's arithmetic (one
-// 16-lane DPP row per 1x128 tile, wave w holding rows 4w .. 4w+3), and writes the codes and
-// the scales with device-scope stores, which go through the XCD's L2 to memory so that
-// workgroups on other XCDs can read them. Slice s of the band is complete when its arrival
-// count cnt[band][s] has reached tiles_n; the activation copies of a slice wait for that and
-// load with device scope.
-// Ordering. Buffer loads and stores report completion in issue order, so the count wait of
-// a slice barrier (every copy complete but the last slice's IPW) also covers the stores a
-// wave issued before those copies: after the barrier, thread 0 publishes them. The staged
-// activation chunks and the count polls arrive by LDS-DMA too, so that the only waits on
-// them are the slice barriers' count waits. A slice that is not complete when its copies are
-// due is polled again with a full wait (the slow path; bounded, with an error word).
-// Counters: cnt [tiles_m][nkb] from word 0 of the caller's 16 KiB counter area, then the
-// done count and the error word at fixed places; the last workgroup to finish resets the
-// counts and the done count to zero.
-// ---------------------------------------------------------------------------------------
-constexpr int kFuseAhead = 5;                  // slices quantised ahead of the one contracted
-constexpr uint32_t kFuseSpinLimit = 1u << 16;  // slow-path polls before giving up (~0.1 s)
-constexpr int kFuseDoneWord = 4094, kFuseErrorWord = 4095;
-
-template <int BM, int NW>
-struct FusedQuant {
-    rsrc_t rx, rq, rs, rc;     // this workgroup's activation, code and scale rows; the band's counts
-    uint32_t xoff, qoff, soff; // per-lane offsets: row t / 16, 16-byte chunk t % 16
-    uint32_t *cnt, *err;
-    uint32_t producers;
-    bool qwave;                // the wave holds rows of the share
-
-    __device__ __forceinline__ FusedQuant(const GemmArgs &g, int64_t m0, int tile_n, int64_t nkb, int wave) {
-        const int rp = (BM + g.tiles_n - 1) / g.tiles_n;
-        const int64_t row0 = m0 + (int64_t)tile_n * rp;
-        int64_t nrows = BM - (int64_t)tile_n * rp;
-        nrows = nrows < rp ? nrows : rp;
-        nrows = nrows < g.M - row0 ? nrows : g.M - row0;
-        nrows = nrows > 0 ? nrows : 0;
-        const int64_t K = g.K;
-        // rows past the share lie outside these ranges: their loads read zero, their stores drop
-        rx = make_rsrc(g.x + row0 * K, nrows * K * 2);
-        rq = make_rsrc(g.aq + row0 * K, nrows * K);
-        rs = make_rsrc(g.sa + row0 * nkb, nrows * nkb * 4);
-        cnt = g.sync + (m0 / BM) * nkb;
-        err = g.sync + kFuseErrorWord;
-        rc = make_rsrc(cnt, nkb * 4);
-        const int t = threadIdx.x, r = t >> 4, c = t & 15;
-        xoff = (uint32_t)((r * K + c * 8) * 2);
-        qoff = (uint32_t)(r * K + c * 8);
-        soff = (uint32_t)(r * nkb * 4);
-        producers = (uint32_t)g.tiles_n;
-        qwave = wave * 4 < nrows;
-    }
-    // LDS-DMA of this lane's 16-byte chunk of slice s to buf + wave * 1 KiB + lane * 16
-    __device__ __forceinline__ void stage(uint8_t *buf, int wave, int s) const {
-        if (qwave)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void *)(buf + wave * 1024), 16, xoff,
-                                                     __builtin_amdgcn_readfirstlane(s * 256), 0, 0);
-    }
-    // quantise the chunk staged in buf (slice s); store its 8 codes and (chunk 0) the scale
-    __device__ __forceinline__ void quantise(const uint8_t *buf, int wave, int lane, int s) const {
-        if (!qwave) return;
-        const u32x4 v = *reinterpret_cast<const u32x4 *>(buf + wave * 1024 + lane * 16);
-        const TileScale ts = tile_scale(row16_max(absmax_bits8(v)));
-        const u32x2 codes = quant8(v, ts);
-        __builtin_amdgcn_raw_buffer_store_b64(codes, rq, qoff, __builtin_amdgcn_readfirstlane(s * 128), kDeviceScope);
-        if ((lane & 15) == 0)
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ts.s), rs, soff, __builtin_amdgcn_readfirstlane(s * 4),
-                                                  kDeviceScope);
-    }
-    // LDS-DMA of slice s's arrival count into the wave's 256-byte poll slot (every lane the same word)
-    __device__ __forceinline__ void poll(uint8_t *slot, int s) const {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, (lds_void *)slot, 4, 0, __builtin_amdgcn_readfirstlane(s * 4), 0,
-                                                 kDeviceScope);
-    }
-    // (a plain LDS read: the poll's landing is ordered by the count waits before each call)
-    __device__ __forceinline__ uint32_t polled(const uint8_t *slot) const {
-        asm volatile("" ::: "memory");
-        return __builtin_amdgcn_readfirstlane(*reinterpret_cast<const uint32_t *>(slot));
-    }
-    // return once slice s of the band is complete; its poll has landed in the slot
-    __device__ __forceinline__ void wait_complete(uint8_t *slot, int s, int lane) const {
-        uint32_t v = polled(slot);
-        if (v >= producers) return;
-        uint32_t n = 0;
-        do {
-            __builtin_amdgcn_s_sleep(8);
-            poll(slot, s);
-            wait_vmcnt<0>();
-            asm volatile("" ::: "memory");
-            v = polled(slot);
-        } while (v < producers && ++n < kFuseSpinLimit);
-        if (v < producers && lane == 0) __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    // one workgroup's rows of slice s are stored (thread 0)
-    __device__ __forceinline__ void publish(int s) const {
-        __hip_atomic_fetch_add(cnt + s, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-};
-
-// stand-in for the kernels without fused act_quant
-struct NoFusedQuant {
-    __device__ __forceinline__ NoFusedQuant(const GemmArgs &, int64_t, int, int64_t, int) {}
-};
 
 // Grouped GEMM work decode, run by the whole workgroup. Expert e has c_e = ceil(rows_e / BM)
 // m-tiles; its c_e * tiles_n tiles are numbered consecutively, experts in order, and within
@@ -531,12 +415,10 @@ __device__ __forceinline__ bool grouped_tile(const GemmArgs &g, uint8_t *scratch
     return true;
 }
 
-template <int BM, int BN, int NW, int WAVES_M, int NSTAGE, int OUT_BF16, int EXACT, int GROUPED, int ROWB,
-          int FUSED = 0>
+template <int BM, int BN, int NW, int WAVES_M, int NSTAGE, int OUT_BF16, int EXACT, int GROUPED, int ROWB>
 __global__ __launch_bounds__(NW * 64) void block_gemm_kernel(GemmArgs g) {
     static_assert(!(GROUPED && ROWB), "per-row weight scales are not grouped");
-    static_assert(!FUSED || (!GROUPED && !ROWB && !EXACT && NW == 8), "fused act_quant: plain FP8-product GEMM");
-    using S = GemmSmem<BM, BN, NSTAGE, NW, ROWB, FUSED>;
+    using S = GemmSmem<BM, BN, NSTAGE, NW, ROWB>;
     constexpr int WAVES_N = NW / WAVES_M;
     static_assert(WAVES_M * WAVES_N == NW, "wave grid");
     constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;    // wave tile
@@ -561,7 +443,7 @@ __global__ __launch_bounds__(NW * 64) void block_gemm_kernel(GemmArgs g) {
     const int64_t nkb = K / G_SLICE;
     const uint8_t *wq = g.wq;
     const float *sw = g.sw;
-    int split = 0, tl = 0, tile_n_of = 0;
+    int split = 0, tl = 0;
     int64_t m0, n0, M;   // first row and column of the tile; M: end of its row range
     if constexpr (!GROUPED) {
         const int tiles = g.tiles_m * g.tiles_n;
@@ -576,7 +458,6 @@ __global__ __launch_bounds__(NW * 64) void block_gemm_kernel(GemmArgs g) {
         const int band_rows = min(g.group, g.tiles_m - band * g.group);
         const int tile_m = band * g.group + in_band % band_rows;
         const int tile_n = in_band / band_rows;
-        tile_n_of = tile_n;
         m0 = (int64_t)tile_m * BM;
         n0 = (int64_t)tile_n * BN;
         M = g.M;
@@ -627,38 +508,8 @@ __global__ __launch_bounds__(NW * 64) void block_gemm_kernel(GemmArgs g) {
         constexpr int COPY_GROUPS = EARLY_BARRIER || PF ? SUB_M - 1 : SUB_M;
         static_assert(COPY_GROUPS >= 1, "row groups per wave");
         constexpr int COPY_PARTS = COPY_GROUPS * SUB_N;
-        const DmaPlan<BM, BN, NSTAGE, NW, FUSED * 16 + ROWB * 8 + GROUPED * 4 + OUT_BF16 * 2 + EXACT, COPY_PARTS, ROWB,
-                      FUSED ? kDeviceScope : 0, FUSED>
-            dma(wave, lane, g.aq, wq, g.sa, sw, m0, n0, M, N, K, nkb, smem + S::DUMMY);
-        using FQ = std::conditional_t<FUSED != 0, FusedQuant<BM, NW>, NoFusedQuant>;
-        [[maybe_unused]] const FQ fz(g, m0, tile_n_of, nkb, wave);
-        if constexpr (FUSED) {
-            static_assert(PF, "fused act_quant runs in the register-prefetch schedule");
-            // Fused prologue: quantise this workgroup's share of the first kFuseAhead slices
-            // (their chunks staged in the stage buffers, not yet in use), stage the next
-            // slice's chunks, publish, then wait until the band's first NSTAGE slices are
-            // complete before their copies are issued.
-            const int npro = (int)min64(kFuseAhead, nkb);
-            for (int s2 = 0; s2 < npro; ++s2) fz.stage(smem + s2 * NW * 1024, wave, s2);
-            if (npro < nkb) fz.stage(smem + S::XSTAGE, wave, npro);
-            wait_vmcnt<0>();
-            asm volatile("" ::: "memory");
-            for (int s2 = 0; s2 < npro; ++s2) fz.quantise(smem + s2 * NW * 1024, wave, lane, s2);
-            wait_vmcnt<0>();      // the stores have completed (and every staged chunk has been read)
-            __syncthreads();
-            if (threadIdx.x == 0)
-                for (int s2 = 0; s2 < npro; ++s2) fz.publish(s2);
-            uint8_t *slot = smem + S::POLL + wave * 256;
-            for (int s2 = 0; s2 < (int)min64(NSTAGE, nkb); ++s2) {
-                fz.poll(slot, s2);
-                wait_vmcnt<0>();
-                asm volatile("" ::: "memory");
-                fz.wait_complete(slot, s2, lane);
-            }
-            // the count of the first slice whose copies go out in the loop, read after its first
-            // barrier (the poll precedes every prologue copy in the count)
-            if (NSTAGE < nkb) fz.poll(slot, NSTAGE);
-        }
+        const DmaPlan<BM, BN, NSTAGE, NW, ROWB * 8 + GROUPED * 4 + OUT_BF16 * 2 + EXACT, COPY_PARTS, ROWB> dma(wave, lane, g.aq, wq, g.sa, sw, m0, n0, M, N,
+                                                                   K, nkb, smem + S::DUMMY);
         // prologue: the first NSTAGE slices in flight
 #pragma unroll
         for (int st = 0; st < NSTAGE; ++st)
@@ -798,19 +649,6 @@ __global__ __launch_bounds__(NW * 64) void block_gemm_kernel(GemmArgs g) {
                             wait_slice<S::IPW, NSTAGE - 2>(later);
                             lds_barrier();
                         }
-                        if constexpr (FUSED) {
-                            // Fused act_quant, before this slice's copies (so that the next slice
-                            // barrier's count wait covers what is issued here). The stores of
-                            // slice kb - 1 + kFuseAhead, issued in the previous slice, are complete.
-                            uint8_t *slot = smem + S::POLL + wave * 256;
-                            if (threadIdx.x == 0 && kb > kbs && kb - 1 + kFuseAhead < kbe) fz.publish(kb - 1 + kFuseAhead);
-                            if (copy_now) fz.wait_complete(slot, kb + NSTAGE, lane);
-                            uint8_t *xs = smem + S::XSTAGE + ((kb - kbs) & 1) * (NW * 1024);
-                            uint8_t *xs_next = smem + S::XSTAGE + (((kb - kbs) & 1) ^ 1) * (NW * 1024);
-                            if (kb + kFuseAhead < kbe) fz.quantise(xs, wave, lane, kb + kFuseAhead);
-                            if (kb + kFuseAhead + 1 < kbe) fz.stage(xs_next, wave, kb + kFuseAhead + 1);
-                            if (kb + NSTAGE + 1 < kbe) fz.poll(slot, kb + NSTAGE + 1);
-                        }
                     }
                 });
             };
@@ -826,26 +664,6 @@ __global__ __launch_bounds__(NW * 64) void block_gemm_kernel(GemmArgs g) {
             });
 #pragma unroll
             for (int j = 0; j < SUB_N; ++j) promote(acc[SUB_M - 1][j], p_prev[j], f_prev[j]);
-            if constexpr (FUSED) {
-                // the last workgroup to finish resets the counts (every workgroup has then passed
-                // its last poll, and its publishes have completed)
-                wait_vmcnt<0>();
-                __syncthreads();
-                int *flag = reinterpret_cast<int *>(smem + S::FLAG);
-                if (threadIdx.x == 0) {
-                    const uint32_t old = __hip_atomic_fetch_add(g.sync + kFuseDoneWord, 1u, __ATOMIC_RELAXED,
-                                                                __HIP_MEMORY_SCOPE_AGENT);
-                    *flag = old == gridDim.x - 1;
-                }
-                __syncthreads();
-                if (*flag) {
-                    const int n = g.tiles_m * (int)nkb;
-                    for (int i = threadIdx.x; i < n; i += NW * 64)
-                        __hip_atomic_store(g.sync + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    if (threadIdx.x == 0)
-                        __hip_atomic_store(g.sync + kFuseDoneWord, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                }
-            }
         } else {
             // fragments of the slice being contracted
             i32x8 wf[SUB_N];
@@ -1362,73 +1180,6 @@ hipError_t launch_block_gemm(const uint8_t *aq, const float *sa, const uint8_t *
         a.part = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + kCounterBytes);
     }
     return dispatch(p, a, out_bf16, exact, stream);
-}
-
-// Fused act_quant + GEMM (FP8 products). The fused kernel is the 128x192 8-wave tile with a
-// workgroup per output tile, launched cooperatively so that every workgroup is resident
-// (the row bands' workgroups wait for each other's quantised slices). It applies when that
-// is the planner's tile without split-K, every row band has at least 4 tiles (so each
-// workgroup quantises at most 32 rows), the tiles fit on the device at once and the band
-// counters fit in the counter area.
-template <int OUT_BF16>
-static constexpr auto fused_kernel = block_gemm_kernel<128, 192, 8, 2, 3, OUT_BF16, 0, 0, 0, 1>;
-
-static int64_t fused_capacity(bool out_bf16) {
-    // resident workgroups of the fused kernel on the current device (cached per device)
-    static std::atomic<int64_t> cap[2][64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-    int64_t c = cap[out_bf16][dev].load(std::memory_order_relaxed);
-    if (c == 0) {
-        int per_cu = 0, cus = 0;
-        const void *k = out_bf16 ? (const void *)fused_kernel<1> : (const void *)fused_kernel<0>;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, 512, 0) != hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-            return 0;
-        c = (int64_t)per_cu * cus;
-        cap[out_bf16][dev].store(c > 0 ? c : -1, std::memory_order_relaxed);
-    }
-    return c > 0 ? c : 0;
-}
-
-static bool fused_applies(const GemmPlan &p, int64_t K, bool out_bf16) {
-    const int64_t nkb = K / G_SLICE;
-    return p.tile == T128x192W8 && p.splits == 1 && nkb >= 1 && p.tiles_n >= 4 &&
-           p.tiles_m * nkb <= kFuseDoneWord && p.tiles_m * p.tiles_n <= fused_capacity(out_bf16);
-}
-
-hipError_t launch_act_quant_gemm(const uint16_t *x, uint8_t *aq, float *sa, const uint8_t *wq, const float *sw,
-                                 void *y, bool out_bf16, bool exact, int64_t M, int64_t N, int64_t K,
-                                 void *workspace, size_t workspace_bytes, hipStream_t stream, int *fused) {
-    if (fused) *fused = 0;
-    if (M == 0) return hipSuccess;
-    if (!exact && N > 0 && workspace && workspace_bytes >= kCounterBytes && env_tile() < 0) {
-        const GemmPlan p = make_plan(M, N, K, false, 0, false);
-        if (fused_applies(p, K, out_bf16)) {
-            GemmArgs a{aq, sa, wq, sw, y, nullptr, nullptr, nullptr, nullptr, M, N, K, 0, 0, 1, 1, 0,
-                       x, static_cast<uint32_t *>(workspace)};
-            a.tiles_m = (int)p.tiles_m;
-            a.tiles_n = (int)p.tiles_n;
-            a.group = choose_group(a.tiles_m, a.tiles_n, 128, 192);
-            void *params[] = {&a};
-            const void *k = out_bf16 ? (const void *)fused_kernel<1> : (const void *)fused_kernel<0>;
-            const hipError_t e = hipLaunchCooperativeKernel(k, dim3((unsigned)(p.tiles_m * p.tiles_n)), dim3(512),
-                                                            params, 0, stream);
-            if (e == hipSuccess) {
-                if (fused) *fused = 1;
-                return e;
-            }
-            (void)hipGetLastError();   // not launched: the two-kernel path below
-        }
-    }
-    const hipError_t e = launch_act_quant(x, aq, sa, M, K, stream);
-    if (e != hipSuccess) return e;
-    return launch_block_gemm(aq, sa, wq, sw, nullptr, y, out_bf16, exact, M, N, K, workspace, workspace_bytes, stream);
-}
-
-size_t act_quant_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, bool out_bf16, bool exact) {
-    const size_t g = gemm_workspace_bytes(M, N, K, out_bf16, exact);
-    return g > kCounterBytes ? g : kCounterBytes;
 }
 
 hipError_t launch_grouped_gemm(const uint8_t *aq, const float *sa, const uint8_t *wq, const float *sw,

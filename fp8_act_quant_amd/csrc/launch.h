@@ -25,16 +25,6 @@ hipError_t launch_block_gemm(const uint8_t *aq, const float *sa, const uint8_t *
                              int64_t K, void *workspace, size_t workspace_bytes, hipStream_t stream);
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, bool out_bf16, bool exact, bool rowb = false);
 
-// act_quant fused into the GEMM: aq, sa = act_quant(x) and y = GEMM(aq, sa, wq, sw), with
-// act_quant's output bytes. One cooperative launch where it applies (FP8 products, the
-// planner's 128x192 tile without split-K, see gemm.hip), else act_quant then the GEMM.
-// *fused (may be NULL) tells which ran. The workspace (act_quant_gemm_workspace_bytes) holds
-// the fused kernel's counters in its 16 KiB counter area; zero before first use, left zero.
-hipError_t launch_act_quant_gemm(const uint16_t *x, uint8_t *aq, float *sa, const uint8_t *wq, const float *sw,
-                                 void *y, bool out_bf16, bool exact, int64_t M, int64_t N, int64_t K,
-                                 void *workspace, size_t workspace_bytes, hipStream_t stream, int *fused);
-size_t act_quant_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, bool out_bf16, bool exact);
-
 // GEMM with per-row scales on both operands: Y = sum over slices kb of
 // (sum_k aq[m,k] bq[n,k]) * sa[m,kb] * sb[n,kb], sb [N, K/128]. Otherwise as launch_block_gemm
 // (no bias); its workspace size is gemm_workspace_bytes(..., rowb = true).

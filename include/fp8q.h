@@ -144,41 +144,6 @@ int fp8_block_gemm_bias(const uint8_t *aq, const float *sa, const uint8_t *wq, c
                         const float *bias, void *y, int y_dtype, int64_t M, int64_t N, int64_t K,
                         void *workspace, size_t workspace_bytes, void *stream);
 
-/* fp8_act_quant_gemm -- act_quant and the block GEMM of linear()'s FP8 branch in one call:
- *   aq, sa = fp8_act_quant(x);  y = fp8_block_gemm(aq, sa, wq, sw).
- * (pomoai.com "DeepSeek-V3", linear(): x, scale = act_quant(x, block_size), then
- * y = fp8_gemm(x, scale, weight, weight.scale).) The outputs are the bytes the two calls
- * produce: aq and sa bit-identical to fp8_act_quant's, y to fp8_block_gemm's with the same
- * plan. Where it applies, the work runs as one cooperative launch in which the workgroups
- * of each output row band quantise the band's activations a few K slices ahead of the
- * contraction and hand them to each other through memory, so that the quantisation's
- * memory traffic overlaps the matrix-unit work; otherwise the two kernels run one after the
- * other. It applies for the FP8-product contraction (bf16 output by default, or
- * FP8Q_GEMM_FP8_PRODUCTS) when the planner's tile is 128x192 without split-K, each row band
- * has at least 4 tiles, every tile fits on the device at once, the band counters fit the
- * counter area and a workspace is given (and no tile is forced for tuning).
- *   x  [M, K] bf16 activations (16-byte aligned); aq [M, K] E4M3 and sa [M, K/128] fp32
- *      outputs (layouts of fp8_act_quant; 16- and 4-byte aligned).
- *   wq, sw, y, y_dtype, M, N, K: as fp8_block_gemm.
- *   workspace / workspace_bytes: device scratch, at least
- *      fp8_act_quant_gemm_workspace_bytes(); its first 16 KiB are counters (the fused
- *      kernel's per row band and K slice, or split-K's) that must be zero before the first
- *      use and that every completed call leaves zero, so zero it once and reuse it. Without
- *      a workspace (NULL / too small) the two-kernel path runs. Word 4095 of the workspace is
- *      an error word: the fused kernel sets it to 1 if a workgroup waited too long (about
- *      0.1 s) for another's slices, which a cooperative launch rules out; then y is not
- *      valid. Calls that may run at the same time must not share a workspace.
- *   fused: optional (may be NULL); set to 1 if the one-launch path was taken, else 0.
- * Errors as fp8_block_gemm; nothing is enqueued on a validation error. */
-int fp8_act_quant_gemm(const uint16_t *x, uint8_t *aq, float *sa, const uint8_t *wq,
-                       const float *sw, void *y, int y_dtype, int64_t M, int64_t N, int64_t K,
-                       void *workspace, size_t workspace_bytes, int *fused, void *stream);
-
-/* Workspace bytes fp8_act_quant_gemm needs for (M, N, K, y_dtype): at least 16 KiB, and
- * what fp8_block_gemm_workspace_bytes asks for where the two-kernel path uses split-K. 0 for
- * invalid arguments. */
-size_t fp8_act_quant_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int y_dtype);
-
 /* fp8_grouped_gemm -- the block-scaled GEMMs of several experts in one launch, for the
  * routed experts of a mixture-of-experts layer: expert e multiplies its own rows of A by its
  * own FP8 weight. (pomoai.com "DeepSeek-V3", MoE section: each token is routed to 8 of
