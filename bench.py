@@ -389,6 +389,18 @@ def main() -> int:
         step(i, evs[i])
     torch.cuda.synchronize()
     t_aq = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e-3
+
+    # act_quant alone, launches back to back over the rotated copies (events only around the
+    # loop): its per-launch time without the dispatch latency a per-launch event pair exposes
+    b2b_n = max(args.steps, 100)
+    a0_ev, a1_ev = TimingEvent(), TimingEvent()
+    torch.cuda.synchronize()
+    a0_ev.record(stream)
+    for i in range(b2b_n):
+        L.check("fp8_act_quant", lib.fp8_act_quant(xs[i % len(xs)], p_aq, p_sa, M, K, sptr))
+    a1_ev.record(stream)
+    torch.cuda.synchronize()
+    t_aq_b2b = a0_ev.elapsed_time(a1_ev) * 1e-3 / b2b_n
     t_gemm = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e-3
 
     flops = 2.0 * M * N * K
@@ -434,6 +446,8 @@ def main() -> int:
             "frac": round(aq_gbs / HBM_PEAK_GBS, 4),
             "avg_launch_us": round(float(t_aq.mean()) * 1e6, 3),
             "algorithmic_bytes_per_launch": aq_bytes,
+            "back_to_back_us": round(t_aq_b2b * 1e6, 3),
+            "back_to_back_frac": round(aq_bytes / t_aq_b2b / 1e9 / HBM_PEAK_GBS, 4),
         },
         "gemm_only_tflops": round(gemm_tflops, 2),
     }
