@@ -966,13 +966,13 @@ struct TileInfo {
 };
 
 static const TileInfo kTiles[T_COUNT] = {
-    {"256x256w8", 256, 256, true, false, 1.84, 10.0, 0, 0, 0},
-    {"256x192w8", 256, 192, true, false, 1.59, 7.5, 0, 0, 0},
-    {"256x128w8", 256, 128, true, true, 1.02, 7.0, 2.04, 5.9, 1},
-    {"128x256w8", 128, 256, true, true, 0.94, 7.0, 2.10, 4.7, 1},
-    {"128x192w8", 128, 192, true, true, 0.78, 5.9, 1.61, 4.7, 3},
-    {"256x128", 256, 128, true, false, 1.22, 7.1, 0, 0, 0},
-    {"128x128", 128, 128, true, true, 0.82, 4.4, 1.36, 4.6, 3},
+    {"256x256w8", 256, 256, true, false, 1.74, 11.1, 0, 0, 0},
+    {"256x192w8", 256, 192, true, false, 1.51, 7.1, 0, 0, 0},
+    {"256x128w8", 256, 128, true, true, 1.00, 7.8, 2.04, 5.9, 1},
+    {"128x256w8", 128, 256, true, true, 0.91, 7.9, 2.10, 4.7, 1},
+    {"128x192w8", 128, 192, true, true, 0.72, 6.2, 1.61, 4.7, 3},
+    {"256x128", 256, 128, true, false, 1.24, 7.5, 0, 0, 0},
+    {"128x128", 128, 128, true, true, 0.80, 5.0, 1.36, 4.6, 3},
     {"128x128s2", 128, 128, false, false, 0.95, 2.8, 0, 0, 0},
 };
 
