@@ -306,7 +306,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=2000)
     ap.add_argument("--copies", type=int, default=10, help="rotated copies of A")
-    ap.add_argument("--cpu-rows", type=int, default=2048, help="token rows in the CPU-baseline sample")
+    ap.add_argument("--cpu-rows", type=int, default=4096, help="token rows in the CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the routed-expert GEMM measurement")
     ap.add_argument("--calibrate-copy", action="store_true",
