@@ -567,7 +567,8 @@ __global__ __launch_bounds__(NW * 64) void block_gemm_kernel(GemmArgs g) {
             // reads and for slice kb + 1's copies, and the workgroup barrier (after which slice
             // kb + 1 is visible and every wave has finished reading slice kb); then row groups
             // 1 .. SUB_M - 1, whose MFMA slots also issue the reads of slice kb + 1 and the
-            // copies of slice kb + NSTAGE. Promotion runs one row group behind, as above.
+            // copies of slice kb + NSTAGE. Promotion runs one row group behind its MFMAs (the last
+            // group of a slice is promoted during the first group of the next).
             static_assert(SUB_M >= 2, "register prefetch needs two row groups");
             i32x8 fa[2][SUB_M], fw[2][SUB_N];
             float sa_r[2][SUB_M];
