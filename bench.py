@@ -1,9 +1,10 @@
 #!/usr/bin/env python3
 """Throughput of the FP8 block-scaled path on one MI355X.
 
-One step = fp8_act_quant(A) -> fp8_block_gemm(Aq, sa, Wq, sw) -> Y on the query
+One step = fp8_act_quant_kmajor(A) -> fp8_block_gemm(Aq, sa, Wq, sw) -> Y on the query
 down-projection workload (A 4096x7168 bf16 tokens, W 1536x7168 pre-quantised to E4M3
-128x128 blocks, Y bf16). Weights are quantised once before timing (offline, as stored
+128x128 blocks, Y bf16). The activation scales are written and read K-block-major
+([K/128, M], the layout in which the GEMM fetches one K slice's scales as whole lines). Weights are quantised once before timing (offline, as stored
 FP8 weights are). Inputs are resident in HBM; A is rotated over several copies so that
 act_quant reads HBM rather than the 256 MB last-level cache. The default warm-up (2000
 untimed steps, ~0.15 s) is sized to the part's clock ramp: under sustained load the
@@ -344,11 +345,11 @@ def main() -> int:
     wq, sw = fq.weight_quant(w)
     del w
     aq = torch.empty((M, K), dtype=torch.float8_e4m3fn, device=dev)
-    sa = torch.empty((M, K // 128), dtype=torch.float32, device=dev)
+    sa = torch.empty((K // 128, M), dtype=torch.float32, device=dev)   # K-block-major scales
     y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream(dev)
     sptr = stream.cuda_stream
-    out_code = L.FP8Q_OUT_BF16
+    out_code = L.FP8Q_OUT_BF16 | L.FP8Q_SA_KMAJOR
     ws_bytes = fq.gemm_workspace_bytes(M, N, K, torch.bfloat16)
     ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device=dev)   # zero-filled before first use
     lib = fq.lib
@@ -359,7 +360,7 @@ def main() -> int:
     def step(i, ev=None):
         if ev is not None:
             ev[0].record(stream)
-        L.check("fp8_act_quant", lib.fp8_act_quant(xs[i % len(xs)], p_aq, p_sa, M, K, sptr))
+        L.check("fp8_act_quant_kmajor", lib.fp8_act_quant_kmajor(xs[i % len(xs)], p_aq, p_sa, M, K, sptr))
         if ev is not None:
             ev[1].record(stream)
         L.check("fp8_block_gemm", lib.fp8_block_gemm(p_aq, p_sa, p_wq, p_sw, p_y, out_code, M, N, K,
@@ -397,7 +398,7 @@ def main() -> int:
     torch.cuda.synchronize()
     a0_ev.record(stream)
     for i in range(b2b_n):
-        L.check("fp8_act_quant", lib.fp8_act_quant(xs[i % len(xs)], p_aq, p_sa, M, K, sptr))
+        L.check("fp8_act_quant_kmajor", lib.fp8_act_quant_kmajor(xs[i % len(xs)], p_aq, p_sa, M, K, sptr))
     a1_ev.record(stream)
     torch.cuda.synchronize()
     t_aq_b2b = a0_ev.elapsed_time(a1_ev) * 1e-3 / b2b_n
@@ -424,7 +425,8 @@ def main() -> int:
         "dtype": "fp8_e4m3",
         "data": "synthetic",
         "config": {"workload": f"{wl.name}: {wl.description}", "M": M, "N": N, "K": K, "out": wl.out_dtype,
-                   "a_copies_rotated": args.copies, "weights": "pre-quantised E4M3 128x128 blocks (untimed)"},
+                   "a_copies_rotated": args.copies, "weights": "pre-quantised E4M3 128x128 blocks (untimed)",
+                   "activation_scales": "K-block-major [K/128, M]"},
         "pct_of_fp8_peak": round(100.0 * value / FP8_PEAK_TFLOPS, 2),
         "roofline": {
             "kernel": "block_gemm_kernel",
@@ -465,6 +467,8 @@ def main() -> int:
         gpu_codes = aq[:r].view(torch.uint8).cpu().numpy()
         cb["gpu_codes_match_oracle_on_sample"] = bool(np.array_equal(gpu_codes, oaq))
         cb["gpu_code_mismatches_on_sample"] = int(np.count_nonzero(gpu_codes != oaq))
+        gpu_scales = sa[:, :r].T.contiguous().view(torch.int32).cpu().numpy()
+        cb["gpu_scales_match_oracle_on_sample"] = bool(np.array_equal(gpu_scales, osa.view(np.int32)))
         result["cpu_baseline"] = cb
     if args.calibrate_copy:
         # a plain streaming kernel of known size (reads and writes COPY_BYTES), untimed

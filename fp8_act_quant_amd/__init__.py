@@ -16,8 +16,8 @@ import math
 import torch
 
 from . import _lib
-from ._lib import (FP8Q_GEMM_EXACT_SLICES, FP8Q_GEMM_FP8_PRODUCTS, FP8Q_OUT_BF16, FP8Q_OUT_F32, Fp8qError,
-                   check, lib)
+from ._lib import (FP8Q_GEMM_EXACT_SLICES, FP8Q_GEMM_FP8_PRODUCTS, FP8Q_OUT_BF16, FP8Q_OUT_F32, FP8Q_SA_KMAJOR,
+                   Fp8qError, check, lib)
 
 BLOCK = 128
 
@@ -45,22 +45,37 @@ def _need(t: torch.Tensor, name: str, dtype, align: int = 16) -> None:
         raise ValueError(f"{name} must be {align}-byte aligned")
 
 
-def act_quant(x: torch.Tensor, block_size: int = BLOCK):
+# K-block-major activation scales are limited to this many (32-bit byte offsets in the GEMM)
+MAX_KMAJOR_SCALES = 1 << 29
+
+
+def act_quant(x: torch.Tensor, block_size: int = BLOCK, scale_layout: str = "row"):
     """Per-token, per-128-channel quantisation of a bf16 activation [..., K].
 
-    Returns ``(q, s)``: q float8_e4m3fn [..., K], s float32 [..., K/128]."""
+    Returns ``(q, s)``: q float8_e4m3fn [..., K], s float32 [..., K/128]. With
+    scale_layout="kmajor" s has the same shape and values but K-block-major storage
+    (``s.movedim(-1, 0)`` is contiguous), the layout in which fp8_gemm reads one K slice's
+    scales as contiguous bytes; it needs fewer than 2^29 scales."""
     if block_size != BLOCK:
         raise ValueError("only block_size=128 is supported")
+    if scale_layout not in ("row", "kmajor"):
+        raise ValueError('scale_layout must be "row" or "kmajor"')
     _need(x, "x", torch.bfloat16)
     K = x.shape[-1]
     if K % BLOCK:
         raise ValueError("the last dimension must be a multiple of 128")
     M = math.prod(x.shape[:-1])
     q = torch.empty(x.shape, dtype=torch.float8_e4m3fn, device=x.device)
-    s = torch.empty((*x.shape[:-1], K // BLOCK), dtype=torch.float32, device=x.device)
     with torch.cuda.device(x.device):
-        check("fp8_act_quant", lib.fp8_act_quant(x.data_ptr(), q.data_ptr(), s.data_ptr(), M, K,
-                                                 _stream(x)))
+        if scale_layout == "row":
+            s = torch.empty((*x.shape[:-1], K // BLOCK), dtype=torch.float32, device=x.device)
+            check("fp8_act_quant", lib.fp8_act_quant(x.data_ptr(), q.data_ptr(), s.data_ptr(), M, K,
+                                                     _stream(x)))
+        else:
+            st = torch.empty((K // BLOCK, *x.shape[:-1]), dtype=torch.float32, device=x.device)
+            check("fp8_act_quant_kmajor", lib.fp8_act_quant_kmajor(x.data_ptr(), q.data_ptr(), st.data_ptr(), M, K,
+                                                                   _stream(x)))
+            s = st.movedim(0, -1)
     return q, s
 
 
@@ -128,10 +143,29 @@ def _auto_workspace(device: torch.device, stream: int, nbytes: int) -> torch.Ten
     return ws
 
 
+def _scale_layout(a_s: torch.Tensor) -> bool:
+    """True for K-block-major activation scales (a_s.movedim(-1, 0) contiguous), False for
+    row-major ones; where both hold (one row or one K slice) the two layouts coincide."""
+    if not isinstance(a_s, torch.Tensor):
+        raise TypeError("a_s must be a torch.Tensor")
+    if a_s.device.type != "cuda":
+        raise ValueError("a_s must be a GPU tensor")
+    if a_s.dtype != torch.float32:
+        raise TypeError(f"a_s must be torch.float32, got {a_s.dtype}")
+    if a_s.numel() and a_s.data_ptr() % 4:
+        raise ValueError("a_s must be 4-byte aligned")
+    if a_s.is_contiguous():
+        return False
+    if a_s.dim() >= 2 and a_s.movedim(-1, 0).is_contiguous():
+        return True
+    raise ValueError("a_s must be contiguous or K-block-major (a_s.movedim(-1, 0) contiguous)")
+
+
 def fp8_gemm(a: torch.Tensor, a_s: torch.Tensor, w: torch.Tensor, w_s: torch.Tensor,
              out_dtype=torch.bfloat16, workspace="auto", out: torch.Tensor | None = None,
              mode: str = "default", bias: torch.Tensor | None = None) -> torch.Tensor:
-    """Block-scaled Y = A . W^T. a: float8_e4m3fn [..., K] with scales [..., K/128];
+    """Block-scaled Y = A . W^T. a: float8_e4m3fn [..., K] with scales [..., K/128]
+    (contiguous, or K-block-major as act_quant(..., scale_layout="kmajor") returns them);
     w: float8_e4m3fn [N, K] with scales [ceil(N/128), K/128]. Returns [..., N] in
     out_dtype (torch.float32 or torch.bfloat16).
 
@@ -147,7 +181,7 @@ def fp8_gemm(a: torch.Tensor, a_s: torch.Tensor, w: torch.Tensor, w_s: torch.Ten
         raise ValueError(f"mode must be one of {sorted(_MODES)}")
     _need(a, "a", torch.float8_e4m3fn)
     _need(w, "w", torch.float8_e4m3fn)
-    _need(a_s, "a_s", torch.float32, align=4)
+    sa_kmajor = _scale_layout(a_s)
     _need(w_s, "w_s", torch.float32, align=4)
     if out_dtype not in (torch.float32, torch.bfloat16):
         raise TypeError("out_dtype must be torch.float32 or torch.bfloat16")
@@ -169,7 +203,7 @@ def fp8_gemm(a: torch.Tensor, a_s: torch.Tensor, w: torch.Tensor, w_s: torch.Ten
         _need(out, "out", out_dtype)
         if tuple(out.shape) != shape:
             raise ValueError(f"out must be {shape}")
-    code = _gemm_code(out_dtype, mode)
+    code = _gemm_code(out_dtype, mode) | (FP8Q_SA_KMAJOR if sa_kmajor else 0)
     ws_ptr, ws_bytes = 0, 0
     if isinstance(workspace, str):
         if workspace != "auto":
@@ -261,7 +295,9 @@ def linear(x: torch.Tensor, weight: torch.Tensor, bias: torch.Tensor | None = No
         return torch.nn.functional.linear(x, weight_dequant(weight, weight_scale), bias)
     if gemm_impl != "fp8":
         raise ValueError('gemm_impl must be "fp8" or "bf16"')
-    q, s = act_quant(x)
+    # K-block-major scales: the GEMM fetches each K slice's scales as whole cache lines
+    M, nkb = math.prod(x.shape[:-1]), x.shape[-1] // BLOCK
+    q, s = act_quant(x, scale_layout="kmajor" if M * nkb < MAX_KMAJOR_SCALES else "row")
     return fp8_gemm(q, s, weight, weight_scale, out_dtype=out_dtype, bias=bias)
 
 

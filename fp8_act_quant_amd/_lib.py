@@ -24,12 +24,14 @@ FP8Q_OUT_F32 = 0
 FP8Q_OUT_BF16 = 1
 FP8Q_GEMM_FP8_PRODUCTS = 0x100
 FP8Q_GEMM_EXACT_SLICES = 0x200
+FP8Q_SA_KMAJOR = 0x1000
 
 # name -> (restype, argtypes); the exports of include/fp8q.h
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
 SIGNATURES = {
     "fp8_act_quant": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _P]),
+    "fp8_act_quant_kmajor": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _P]),
     "fp8_weight_quant": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _P]),
     "fp8_weight_dequant": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _P]),
     "fp8_block_gemm": (ctypes.c_int, [_P, _P, _P, _P, _P, ctypes.c_int, _I64, _I64, _I64, _P,

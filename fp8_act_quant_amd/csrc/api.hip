@@ -20,6 +20,8 @@ constexpr int64_t kMaxWeightBlockRows = 65535;
 constexpr int64_t kMaxGemmK = (int64_t)1 << 24;
 // grid dimensions of the two-dimensional launches
 constexpr int64_t kMaxGridX = 0x7FFFFFFF, kMaxGridY = 65535;
+// K-block-major activation scales are addressed with 32-bit byte offsets: M * K/128 < 2^29
+constexpr int64_t kMaxKmajorScales = (int64_t)1 << 29;
 
 bool misaligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
 
@@ -59,7 +61,17 @@ int fp8_act_quant(const uint16_t *x, uint8_t *q, float *s, int64_t M, int64_t K,
     if (!x || !q || !s) return FP8Q_ERR_NULL;
     if (misaligned(x, 16) || misaligned(q, 16) || misaligned(s, 4)) return FP8Q_ERR_ALIGN;
     if (int e = check_device()) return e;
-    return finish(fp8q::launch_act_quant(x, q, s, M, K, static_cast<hipStream_t>(stream)));
+    return finish(fp8q::launch_act_quant(x, q, s, M, K, false, static_cast<hipStream_t>(stream)));
+}
+
+int fp8_act_quant_kmajor(const uint16_t *x, uint8_t *q, float *s, int64_t M, int64_t K, void *stream) {
+    if (int e = shape_ok(M, K)) return e;
+    if (K > 0 && M >= kMaxKmajorScales / (K / kBlock)) return FP8Q_ERR_SHAPE;
+    if (M == 0 || K == 0) return FP8Q_OK;
+    if (!x || !q || !s) return FP8Q_ERR_NULL;
+    if (misaligned(x, 16) || misaligned(q, 16) || misaligned(s, 4)) return FP8Q_ERR_ALIGN;
+    if (int e = check_device()) return e;
+    return finish(fp8q::launch_act_quant(x, q, s, M, K, true, static_cast<hipStream_t>(stream)));
 }
 
 int fp8_weight_quant(const uint16_t *w, uint8_t *q, float *s, int64_t N, int64_t K, void *stream) {
@@ -91,13 +103,15 @@ int fp8_block_gemm_bias(const uint8_t *aq, const float *sa, const uint8_t *wq, c
                         void *y, int y_dtype, int64_t M, int64_t N, int64_t K, void *workspace,
                         size_t workspace_bytes, void *stream) {
     const int dtype = y_dtype & 0xFF;
-    const int mode = y_dtype & ~0xFF;
+    const bool sa_kmajor = (y_dtype & FP8Q_SA_KMAJOR) != 0;
+    const int mode = y_dtype & ~0xFF & ~FP8Q_SA_KMAJOR;
     if (dtype != FP8Q_OUT_F32 && dtype != FP8Q_OUT_BF16) return FP8Q_ERR_DTYPE;
     if (mode != 0 && mode != FP8Q_GEMM_FP8_PRODUCTS && mode != FP8Q_GEMM_EXACT_SLICES) return FP8Q_ERR_DTYPE;
     if (int e = shape_ok(M, K)) return e;
     if (int e = shape_ok(N, K)) return e;
     if (M > 0 && N > kMaxElems / M) return FP8Q_ERR_SHAPE;
     if (K > kMaxGemmK) return FP8Q_ERR_SHAPE;
+    if (sa_kmajor && K > 0 && M >= kMaxKmajorScales / (K / kBlock)) return FP8Q_ERR_SHAPE;
     if (M == 0 || N == 0) return FP8Q_OK;
     if (!y) return FP8Q_ERR_NULL;
     if (K > 0 && (!aq || !sa || !wq || !sw)) return FP8Q_ERR_NULL;
@@ -109,8 +123,8 @@ int fp8_block_gemm_bias(const uint8_t *aq, const float *sa, const uint8_t *wq, c
     if (int e = check_device()) return e;
     // default contraction: exact slices for fp32 output, the FP8 matrix unit for bf16 output
     const bool exact = mode == FP8Q_GEMM_EXACT_SLICES || (mode == 0 && dtype == FP8Q_OUT_F32);
-    return finish(fp8q::launch_block_gemm(aq, sa, wq, sw, bias, y, dtype == FP8Q_OUT_BF16, exact, M, N, K,
-                                          workspace, workspace_bytes, static_cast<hipStream_t>(stream)));
+    return finish(fp8q::launch_block_gemm(aq, sa, wq, sw, bias, y, dtype == FP8Q_OUT_BF16, exact, sa_kmajor, M, N,
+                                          K, workspace, workspace_bytes, static_cast<hipStream_t>(stream)));
 }
 
 int fp8_grouped_gemm(const uint8_t *aq, const float *sa, const uint8_t *wq, const float *sw, const int64_t *offsets,
@@ -198,7 +212,7 @@ size_t fp8_block_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int y_dty
     if (M <= 0 || N <= 0 || K <= 0 || (K % kBlock) != 0 || K > kMaxGemmK) return 0;
     if (N > kMaxElems / M || shape_ok(M, K) || shape_ok(N, K)) return 0;
     const int dtype = y_dtype & 0xFF;
-    const int mode = y_dtype & ~0xFF;
+    const int mode = y_dtype & ~0xFF & ~FP8Q_SA_KMAJOR;   // (the scale layout does not change the plan)
     if (dtype != FP8Q_OUT_F32 && dtype != FP8Q_OUT_BF16) return 0;
     if (mode != 0 && mode != FP8Q_GEMM_FP8_PRODUCTS && mode != FP8Q_GEMM_EXACT_SLICES) return 0;
     const bool exact = mode == FP8Q_GEMM_EXACT_SLICES || (mode == 0 && dtype == FP8Q_OUT_F32);

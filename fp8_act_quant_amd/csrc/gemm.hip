@@ -231,16 +231,28 @@ struct DmaPlan {
     rsrc_t ra, rw, rsa, rsw;
     uint32_t off[S::IPW];
     int w;
+    int sa_step;   // bytes between the activation scales of consecutive K slices
     uint8_t *dummy;
 
+    // sa_ld: 0 for row-major activation scales [M, nkb], else the row count of K-block-major
+    // scales [nkb, sa_ld] (one slice's scales of consecutive rows contiguous)
     __device__ __forceinline__ DmaPlan(int wave, int lane, const uint8_t *aq, const uint8_t *wq, const float *sa,
                                        const float *sw, int64_t m0, int64_t n0, int64_t M, int64_t N, int64_t K,
-                                       int64_t nkb, uint8_t *smem_dummy) {
+                                       int64_t nkb, int64_t sa_ld, uint8_t *smem_dummy) {
         const int64_t rows_a = (M - m0) < BM ? (M - m0) : BM;
         const int64_t rows_w = (N - n0) < BN ? (N - n0) : BN;
         ra = make_rsrc(aq + m0 * K, rows_a * K);
         rw = make_rsrc(wq + n0 * K, rows_w * K);
-        rsa = make_rsrc(sa + m0 * nkb, rows_a * nkb * 4);
+        // K-block-major: rows past M of a tile read the next slice's first scales (or, in
+        // the last slice, zero); they only feed outputs that are never stored
+        if (sa_ld) {
+            rsa = make_rsrc(sa + m0, (nkb * sa_ld - m0) * 4);
+            sa_step = (int)(sa_ld * 4);
+        } else {
+            rsa = make_rsrc(sa + m0 * nkb, rows_a * nkb * 4);
+            sa_step = 4;
+        }
+        const int sa_row = sa_ld ? 4 : (int)(nkb * 4);
         if constexpr (ROWB) {
             rsw = make_rsrc(sw + n0 * nkb, rows_w * nkb * 4);
         } else {
@@ -263,7 +275,7 @@ struct DmaPlan {
 #pragma unroll
         for (int t = 0; t < S::SA_INSTR; ++t) {
             const int b = NW * t + w;
-            off[S::A_INSTR + S::W_INSTR + t] = b < S::SA_BLOCKS ? (uint32_t)((64 * b + lane) * nkb * 4) : 0u;
+            off[S::A_INSTR + S::W_INSTR + t] = b < S::SA_BLOCKS ? (uint32_t)((64 * b + lane) * sa_row) : 0u;
         }
         if constexpr (ROWB) {
 #pragma unroll
@@ -278,7 +290,7 @@ struct DmaPlan {
 
     // instruction I (of IPW) of the copies of slice kb into stage buffer `base`; I is a
     // constant wherever this is inlined (the loops that call it are unrolled)
-    __device__ __forceinline__ void issue_one(uint8_t *base, int koff, int soff, int I) const {
+    __device__ __forceinline__ void issue_one(uint8_t *base, int koff, int soff, int saoff, int I) const {
         if (I < S::A_INSTR) {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(base + 8 * (NW * I + w) * G_SLICE), 16, off[I],
                                                      koff, 0, 0);
@@ -289,7 +301,7 @@ struct DmaPlan {
         } else if (I < S::IPW - S::SW_INSTR) {
             const int b = NW * (I - S::A_INSTR - S::W_INSTR) + w;
             uint8_t *dst = b < S::SA_BLOCKS ? base + S::A_BYTES + S::W_BYTES + b * 256 : dummy;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_void *)dst, 4, off[I], soff, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_void *)dst, 4, off[I], saoff, 0, 0);
         } else if (ROWB) {
             const int b = NW * (I - (S::IPW - S::SW_INSTR)) + w;
             uint8_t *dst = b < S::SB_BLOCKS ? base + S::A_BYTES + S::W_BYTES + S::SA_BYTES + b * 256 : dummy;
@@ -304,8 +316,9 @@ struct DmaPlan {
     __device__ __forceinline__ void issue(uint8_t *base, int64_t kb) const {
         const int koff = __builtin_amdgcn_readfirstlane((int)(kb * G_SLICE));
         const int soff = __builtin_amdgcn_readfirstlane((int)(kb * 4));
+        const int saoff = __builtin_amdgcn_readfirstlane((int)kb * sa_step);
 #pragma unroll
-        for (int I = 0; I < S::IPW; ++I) issue_one(base, koff, soff, I);
+        for (int I = 0; I < S::IPW; ++I) issue_one(base, koff, soff, saoff, I);
     }
 
     // part g of NG (g a constant after unrolling) of the copies of slice kb: instructions
@@ -316,9 +329,10 @@ struct DmaPlan {
         // would make the compiler wrap each copy in a per-value loop)
         const int koff = __builtin_amdgcn_readfirstlane((int)(kb * G_SLICE));
         const int soff = __builtin_amdgcn_readfirstlane((int)(kb * 4));
+        const int saoff = __builtin_amdgcn_readfirstlane((int)kb * sa_step);
 #pragma unroll
         for (int c = 0; c < PER; ++c)
-            if (g * PER + c < S::IPW) issue_one(base, koff, soff, g * PER + c);
+            if (g * PER + c < S::IPW) issue_one(base, koff, soff, saoff, g * PER + c);
     }
 };
 
@@ -338,6 +352,7 @@ struct GemmArgs {
     int64_t M, N, K;
     int tiles_m, tiles_n, group, splits;
     int experts;
+    int sa_kmajor;      // plain GEMM: sa is K-block-major [K/128, M] (M * K/128 < 2^29)
 };
 
 constexpr int kMaxExperts = (int)kMaxGroupedExperts;
@@ -509,7 +524,7 @@ __global__ __launch_bounds__(NW * 64) void block_gemm_kernel(GemmArgs g) {
         static_assert(COPY_GROUPS >= 1, "row groups per wave");
         constexpr int COPY_PARTS = COPY_GROUPS * SUB_N;
         const DmaPlan<BM, BN, NSTAGE, NW, ROWB * 8 + GROUPED * 4 + OUT_BF16 * 2 + EXACT, COPY_PARTS, ROWB> dma(wave, lane, g.aq, wq, g.sa, sw, m0, n0, M, N,
-                                                                   K, nkb, smem + S::DUMMY);
+                                                                   K, nkb, GROUPED || !g.sa_kmajor ? 0 : M, smem + S::DUMMY);
         // prologue: the first NSTAGE slices in flight
 #pragma unroll
         for (int st = 0; st < NSTAGE; ++st)
@@ -1162,7 +1177,7 @@ hipError_t launch_rowwise_gemm(const uint8_t *aq, const float *sa, const uint8_t
                                size_t workspace_bytes, hipStream_t stream) {
     if (M == 0 || N == 0) return hipSuccess;
     const GemmPlan p = make_plan(M, N, K, exact, workspace ? workspace_bytes : 0, false, true);
-    GemmArgs a{aq, sa, bq, sb, y, nullptr, nullptr, nullptr, nullptr, M, N, K, 0, 0, 1, 1, 0};
+    GemmArgs a{aq, sa, bq, sb, y, nullptr, nullptr, nullptr, nullptr, M, N, K, 0, 0, 1, 1, 0, 0};
     if (p.splits > 1) {
         a.count = static_cast<uint32_t *>(workspace);
         a.part = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + kCounterBytes);
@@ -1171,11 +1186,12 @@ hipError_t launch_rowwise_gemm(const uint8_t *aq, const float *sa, const uint8_t
 }
 
 hipError_t launch_block_gemm(const uint8_t *aq, const float *sa, const uint8_t *wq, const float *sw,
-                             const float *bias, void *y, bool out_bf16, bool exact, int64_t M, int64_t N, int64_t K,
-                             void *workspace, size_t workspace_bytes, hipStream_t stream) {
+                             const float *bias, void *y, bool out_bf16, bool exact, bool sa_kmajor, int64_t M,
+                             int64_t N, int64_t K, void *workspace, size_t workspace_bytes, hipStream_t stream) {
     if (M == 0 || N == 0) return hipSuccess;
+    if (sa_kmajor && M * (K / G_SLICE) >= ((int64_t)1 << 29)) return hipErrorInvalidValue;
     const GemmPlan p = make_plan(M, N, K, exact, workspace ? workspace_bytes : 0, false);
-    GemmArgs a{aq, sa, wq, sw, y, bias, nullptr, nullptr, nullptr, M, N, K, 0, 0, 1, 1, 0};
+    GemmArgs a{aq, sa, wq, sw, y, bias, nullptr, nullptr, nullptr, M, N, K, 0, 0, 1, 1, 0, sa_kmajor ? 1 : 0};
     if (p.splits > 1) {
         a.count = static_cast<uint32_t *>(workspace);
         a.part = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + kCounterBytes);
@@ -1189,7 +1205,7 @@ hipError_t launch_grouped_gemm(const uint8_t *aq, const float *sa, const uint8_t
     if (rows == 0 || N == 0) return hipSuccess;
     // Few tiles are instantiated for the grouped kernel: BM = 128 keeps the padding of each
     // expert's last m-tile small; BN = 256 for wide weights, 192 otherwise.
-    GemmArgs a{aq, sa, wq, sw, y, nullptr, nullptr, nullptr, offsets, rows, N, K, 0, 0, 1, 1, (int)experts};
+    GemmArgs a{aq, sa, wq, sw, y, nullptr, nullptr, nullptr, offsets, rows, N, K, 0, 0, 1, 1, (int)experts, 0};
     if (exact) return launch_cfg<128, 192, 8, 2, 3, 1, 1>(a, out_bf16, 1, stream);
     if (N >= 1024) return launch_cfg<128, 256, 8, 2, 3, 0, 1>(a, out_bf16, 1, stream);
     return launch_cfg<128, 192, 8, 2, 3, 0, 1>(a, out_bf16, 1, stream);

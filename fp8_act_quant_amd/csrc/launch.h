@@ -8,7 +8,8 @@
 
 namespace fp8q {
 
-hipError_t launch_act_quant(const uint16_t *x, uint8_t *q, float *s, int64_t M, int64_t K,
+// kmajor: scales written K-block-major, s[kb * M + m] (M * K/128 < 2^32), else s[m * K/128 + kb]
+hipError_t launch_act_quant(const uint16_t *x, uint8_t *q, float *s, int64_t M, int64_t K, bool kmajor,
                             hipStream_t stream);
 hipError_t launch_weight_quant(const uint16_t *w, uint8_t *q, float *s, int64_t N, int64_t K,
                                hipStream_t stream);
@@ -20,9 +21,10 @@ hipError_t launch_weight_dequant(const uint8_t *q, const float *s, uint16_t *w, 
 // unit. bias (fp32 [N], may be NULL) is added in fp32 before the output rounding. The workspace (may be NULL) is used for a split-K schedule when workspace_bytes >=
 // gemm_workspace_bytes(M, N, K, out_bf16, exact); it must hold zeros in its counter area
 // before its first use, and every call leaves them zero.
+// sa_kmajor: sa is K-block-major [K/128, M] (M * K/128 < 2^29), else row-major [M, K/128].
 hipError_t launch_block_gemm(const uint8_t *aq, const float *sa, const uint8_t *wq, const float *sw,
-                             const float *bias, void *y, bool out_bf16, bool exact, int64_t M, int64_t N,
-                             int64_t K, void *workspace, size_t workspace_bytes, hipStream_t stream);
+                             const float *bias, void *y, bool out_bf16, bool exact, bool sa_kmajor, int64_t M,
+                             int64_t N, int64_t K, void *workspace, size_t workspace_bytes, hipStream_t stream);
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, bool out_bf16, bool exact, bool rowb = false);
 
 // GEMM with per-row scales on both operands: Y = sum over slices kb of

@@ -21,56 +21,123 @@ namespace fp8q {
 // consecutive tiles, grid-stride, and issues the loads of its next group before
 // quantising the current one, so that two groups' loads per lane are in flight and the
 // stream never drains between groups.
+// The K-block-major variant writes the scale of row m, K slice kb to s[kb * M + m] (the
+// layout in which one K slice's scales of consecutive tokens are contiguous). Its groups
+// are 64 consecutive rows of one K slice instead (group g: rows 64 (g / nkb) .., slice
+// g % nkb), so that the four tiles of a load instruction are four consecutive rows and
+// each instruction's scale stores fill 16 contiguous bytes; every tile is still one
+// 256-byte run of x. The quotient g / nkb is formed by multiplication with a precomputed
+// reciprocal (Granlund and Montgomery, "Division by invariant integers using
+// multiplication", 1994, the round-up method for unsigned N-bit division), exact for every
+// 32-bit g.
 // ------------------------------------------------------------------------------------
 constexpr int AQ_THREADS = 256;
 constexpr int AQ_UNROLL = 4;
 constexpr int AQ_TILES_PER_WAVE = 4 * AQ_UNROLL;
 constexpr int AQ_TILES_PER_GROUP = AQ_TILES_PER_WAVE * (AQ_THREADS / 64);
 
-__device__ __forceinline__ void aq_load(const u32x4 *__restrict__ x, int64_t tile0, int j, int64_t n_tiles,
+// Unsigned 32-bit division by an invariant d >= 1: with l = ceil(log2 d),
+// magic = floor(2^32 (2^l - d) / d) + 1, t1 = hi32(magic * n), the quotient is
+// (t1 + ((n - t1) >> min(l, 1))) >> max(l - 1, 0).
+struct DivU32 {
+    uint32_t d, magic;
+    int sh1, sh2;
+    __device__ __forceinline__ uint32_t div(uint32_t n) const {
+        const uint32_t t1 = __umulhi(magic, n);
+        return (t1 + ((n - t1) >> sh1)) >> sh2;
+    }
+};
+
+static DivU32 make_div(uint32_t d) {
+    int l = 0;
+    while (l < 32 && (uint64_t(1) << l) < d) ++l;
+    DivU32 r;
+    r.d = d;
+    r.magic = (uint32_t)(((uint64_t(1) << 32) * ((uint64_t(1) << l) - d)) / d + 1);
+    r.sh1 = l < 1 ? l : 1;
+    r.sh2 = l > 1 ? l - 1 : 0;
+    return r;
+}
+
+// The AQ_UNROLL tiles of one lane in group g: tile t0 + u * step (u = 0 .. AQ_UNROLL-1),
+// which exists while idx0 + 4 u < lim. Row-major: 64 consecutive flat tiles (idx = tile
+// number). K-block-major: 64 consecutive rows of one K slice (idx = row, the scale goes
+// to s[kb * M + row]).
+struct AqLane {
+    int64_t t0, step, idx0, lim, s0;   // s0: scale index of the first tile (its step is 4)
+};
+
+template <int KMAJOR>
+__device__ __forceinline__ AqLane aq_lane(int64_t g, int64_t my, int64_t n_tiles, int64_t M, const DivU32 &by_nkb) {
+    AqLane r;
+    if constexpr (KMAJOR) {
+        const int64_t nkb = by_nkb.d;
+        const int64_t mb = by_nkb.div((uint32_t)g), kb = g - mb * nkb;
+        const int64_t m0 = mb * AQ_TILES_PER_GROUP + my;
+        r.t0 = m0 * nkb + kb;
+        r.step = 4 * nkb;
+        r.idx0 = m0;
+        r.lim = M;
+        r.s0 = kb * M + m0;
+    } else {
+        r.t0 = g * AQ_TILES_PER_GROUP + my;
+        r.step = 4;
+        r.idx0 = r.t0;
+        r.lim = n_tiles;
+        r.s0 = r.t0;
+    }
+    return r;
+}
+
+__device__ __forceinline__ void aq_load(const u32x4 *__restrict__ x, const AqLane &l, int j, bool any,
                                         u32x4 (&v)[AQ_UNROLL]) {
 #pragma unroll
     for (int u = 0; u < AQ_UNROLL; ++u) {
-        const int64_t t = tile0 + 4 * u;
-        v[u] = (t < n_tiles) ? __builtin_nontemporal_load(&x[t * 16 + j]) : u32x4{0, 0, 0, 0};
+        const int64_t t = l.t0 + u * l.step;
+        v[u] = (any && l.idx0 + 4 * u < l.lim) ? __builtin_nontemporal_load(&x[t * 16 + j]) : u32x4{0, 0, 0, 0};
     }
 }
 
+// KMAJOR: scales K-block-major (s[kb * M + m]); the group count is below 2^32 there
+template <int KMAJOR>
 __global__ __launch_bounds__(AQ_THREADS) void act_quant_kernel(const u32x4 *__restrict__ x,
                                                                u32x2 *__restrict__ q,
                                                                float *__restrict__ s,
-                                                               int64_t n_tiles) {
+                                                               int64_t n_tiles, DivU32 by_nkb, int64_t M) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int j = lane & 15;
     const int64_t my = wave * AQ_TILES_PER_WAVE + (lane >> 4);   // this lane's first tile within a group
-    const int64_t n_groups = (n_tiles + AQ_TILES_PER_GROUP - 1) / AQ_TILES_PER_GROUP;
+    const int64_t n_groups = KMAJOR ? (M + AQ_TILES_PER_GROUP - 1) / AQ_TILES_PER_GROUP * by_nkb.d
+                                    : (n_tiles + AQ_TILES_PER_GROUP - 1) / AQ_TILES_PER_GROUP;
 
     int64_t g = blockIdx.x;
     u32x4 v[AQ_UNROLL];
-    aq_load(x, g * AQ_TILES_PER_GROUP + my, j, n_tiles, v);
+    AqLane cur = aq_lane<KMAJOR>(g, my, n_tiles, M, by_nkb);
+    aq_load(x, cur, j, g < n_groups, v);
     while (g < n_groups) {
         const int64_t gn = g + gridDim.x;
+        const AqLane nxt = aq_lane<KMAJOR>(gn < n_groups ? gn : g, my, n_tiles, M, by_nkb);
         u32x4 vn[AQ_UNROLL];
-        aq_load(x, gn * AQ_TILES_PER_GROUP + my, j, gn < n_groups ? n_tiles : 0, vn);
-        const int64_t tile0 = g * AQ_TILES_PER_GROUP + my;
+        aq_load(x, nxt, j, gn < n_groups, vn);
 #pragma unroll
         for (int u = 0; u < AQ_UNROLL; ++u) {
-            const int64_t t = tile0 + 4 * u;
+            const int64_t t = cur.t0 + u * cur.step;
             const uint32_t amax = row16_max(absmax_bits8(v[u]));
             const TileScale ts = tile_scale(amax);
             const u32x2 codes = quant8(v[u], ts);
-            if (t < n_tiles) {
+            if (cur.idx0 + 4 * u < cur.lim) {
                 // an ordinary (cache-allocating) store: the codes (1 B per element) are read
                 // by the GEMM right after, and staying in the 256 MB MALL saves it the HBM
                 // round trip (measured: GEMM -8%, act_quant +5%, step -2.4%); the bf16 input
                 // is streamed with non-temporal loads
                 q[t * 16 + j] = codes;
-                if (j == 0) s[t] = ts.s;
+                if (j == 0) s[cur.s0 + 4 * u] = ts.s;
             }
         }
 #pragma unroll
         for (int u = 0; u < AQ_UNROLL; ++u) v[u] = vn[u];
+        cur = nxt;
         g = gn;
     }
 }
@@ -85,15 +152,23 @@ static int aq_wgs_per_cu() {
     return v;
 }
 
-hipError_t launch_act_quant(const uint16_t *x, uint8_t *q, float *s, int64_t M, int64_t K,
+hipError_t launch_act_quant(const uint16_t *x, uint8_t *q, float *s, int64_t M, int64_t K, bool kmajor,
                             hipStream_t stream) {
     const int64_t n_tiles = M * (K / kBlock);
     if (n_tiles == 0) return hipSuccess;
-    const int64_t groups = (n_tiles + AQ_TILES_PER_GROUP - 1) / AQ_TILES_PER_GROUP;
+    // (K-block-major groups: 64 rows of one K slice, numbered below 2^32)
+    const int64_t groups = kmajor ? (M + AQ_TILES_PER_GROUP - 1) / AQ_TILES_PER_GROUP * (K / kBlock)
+                                  : (n_tiles + AQ_TILES_PER_GROUP - 1) / AQ_TILES_PER_GROUP;
+    if (kmajor && groups > 0xFFFFFFFFll) return hipErrorInvalidValue;
     const int64_t cap = (int64_t)256 * aq_wgs_per_cu();
     const int64_t blocks = groups < cap ? groups : cap;
-    hipLaunchKernelGGL(act_quant_kernel, dim3((unsigned)blocks), dim3(AQ_THREADS), 0, stream,
-                       reinterpret_cast<const u32x4 *>(x), reinterpret_cast<u32x2 *>(q), s, n_tiles);
+    const DivU32 by_nkb = make_div(kmajor ? (uint32_t)(K / kBlock) : 1u);   // (unused in row-major order)
+    if (kmajor)
+        hipLaunchKernelGGL(act_quant_kernel<1>, dim3((unsigned)blocks), dim3(AQ_THREADS), 0, stream,
+                           reinterpret_cast<const u32x4 *>(x), reinterpret_cast<u32x2 *>(q), s, n_tiles, by_nkb, M);
+    else
+        hipLaunchKernelGGL(act_quant_kernel<0>, dim3((unsigned)blocks), dim3(AQ_THREADS), 0, stream,
+                           reinterpret_cast<const u32x4 *>(x), reinterpret_cast<u32x2 *>(q), s, n_tiles, by_nkb, M);
     return hipGetLastError();
 }
 

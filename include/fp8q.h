@@ -77,6 +77,14 @@ extern "C" {
 #define FP8Q_GEMM_FP8_PRODUCTS 0x100
 #define FP8Q_GEMM_EXACT_SLICES 0x200
 
+/* Layout flag of fp8_block_gemm / fp8_block_gemm_bias, OR-ed into y_dtype: the activation
+ * scales sa are K-block-major, [K/128, M] with sa[kb * M + m] (the layout of
+ * fp8_act_quant_kmajor), instead of row-major [M, K/128]. The values are the same; in this
+ * layout the scales of one K slice for consecutive rows are contiguous, so the GEMM fetches
+ * them as whole cache lines. Requires M * (K/128) < 2^29 (FP8Q_ERR_SHAPE otherwise).
+ * fp8_grouped_gemm and fp8_rowwise_gemm take row-major scales only (FP8Q_ERR_DTYPE). */
+#define FP8Q_SA_KMAJOR 0x1000
+
 /* fp8_act_quant -- per-token, per-128-channel activation quantisation.
  * (pomoai.com "DeepSeek-V3", FP8 section: dynamic activation quantisation per token per
  * 128 channels; act_quant in the linear() listing.)
@@ -86,6 +94,14 @@ extern "C" {
  *                                               4-byte aligned.
  * Every code and scale is bit-identical to the definition above. */
 int fp8_act_quant(const uint16_t *x, uint8_t *q, float *s, int64_t M, int64_t K, void *stream);
+
+/* fp8_act_quant_kmajor -- fp8_act_quant (same passage, same codes and scale values) with the
+ * scales written K-block-major:
+ *   s  [K/128, M] fp32; s[kb * M + m] is the scale of x[m, 128*kb : 128*kb + 128].
+ *                                               4-byte aligned.
+ * The input of fp8_block_gemm with FP8Q_SA_KMAJOR. Requires M * (K/128) < 2^29
+ * (FP8Q_ERR_SHAPE otherwise); other arguments and errors as fp8_act_quant. */
+int fp8_act_quant_kmajor(const uint16_t *x, uint8_t *q, float *s, int64_t M, int64_t K, void *stream);
 
 /* fp8_weight_quant -- 128x128 block quantisation of a weight matrix.
  * (pomoai.com "DeepSeek-V3", FP8 section: FP8 weights in 128x128 blocks, one float32
@@ -108,11 +124,13 @@ int fp8_weight_dequant(const uint8_t *q, const float *s, uint16_t *w, int64_t N,
                        void *stream);
 
 /* fp8_block_gemm -- Y = A . W^T on block-quantised operands with per-slice promotion.
- * y_dtype = FP8Q_OUT_F32 or FP8Q_OUT_BF16, optionally OR-ed with one FP8Q_GEMM_* mode.
+ * y_dtype = FP8Q_OUT_F32 or FP8Q_OUT_BF16, optionally OR-ed with one FP8Q_GEMM_* mode and
+ * with FP8Q_SA_KMAJOR.
  * (pomoai.com "DeepSeek-V3", linear(): fp8_gemm(x, scale, weight, weight.scale);
  * qdgithub.com 25/317: FP8 products inside each block, dequantisation outside the matrix
  * units; 88811315.cn 75335: FP8 partials promoted into an FP32 accumulator.)
- *   aq [M, K] E4M3 activations, sa [M, K/128] fp32   (layout of fp8_act_quant)
+ *   aq [M, K] E4M3 activations, sa [M, K/128] fp32   (layout of fp8_act_quant), or
+ *      with FP8Q_SA_KMAJOR sa [K/128, M]            (layout of fp8_act_quant_kmajor)
  *   wq [N, K] E4M3 weights,     sw [ceil(N/128), K/128] fp32 (layout of fp8_weight_quant)
  *   y  [M, N] output, fp32 (y_dtype = FP8Q_OUT_F32) or bf16 bits (FP8Q_OUT_BF16, RNE of
  *      the fp32 accumulator). With K = 0 the output is all zeros.

@@ -78,6 +78,22 @@ def test_act_quant_validation(lib):
     assert lib.fp8_act_quant(FAKE, FAKE, FAKE, 1 << 40, 1 << 20, None) == L.FP8Q_ERR_SHAPE
 
 
+def test_act_quant_kmajor_validation(lib):
+    """The K-block-major variant validates like fp8_act_quant, and also rejects grids of
+    2^29 or more scales (their byte offsets would not fit the GEMM's 32-bit addressing)."""
+    from fp8_act_quant_amd import _lib as L
+    f = lib.fp8_act_quant_kmajor
+    assert f(FAKE, FAKE, FAKE, 4, 100, None) == L.FP8Q_ERR_SHAPE
+    assert f(FAKE, FAKE, FAKE, -1, 128, None) == L.FP8Q_ERR_SHAPE
+    assert f(None, FAKE, FAKE, 4, 128, None) == L.FP8Q_ERR_NULL
+    assert f(FAKE, FAKE, None, 4, 128, None) == L.FP8Q_ERR_NULL
+    assert f(FAKE, FAKE + 4, FAKE, 4, 128, None) == L.FP8Q_ERR_ALIGN
+    assert f(FAKE, FAKE, FAKE + 2, 4, 128, None) == L.FP8Q_ERR_ALIGN
+    assert f(None, None, None, 0, 128, None) == L.FP8Q_OK
+    assert f(FAKE, FAKE, FAKE, 1 << 23, 64 * 128, None) == L.FP8Q_ERR_SHAPE      # exactly 2^29 scales
+    assert f(FAKE, FAKE, FAKE, 1 << 29, 128, None) == L.FP8Q_ERR_SHAPE
+
+
 def test_weight_quant_and_dequant_validation(lib):
     from fp8_act_quant_amd import _lib as L
     for fn in (lib.fp8_weight_quant,):
@@ -121,6 +137,17 @@ def test_block_gemm_validation(lib):
     assert lib.fp8_block_gemm_workspace_bytes(4096, 576, 7168, L.FP8Q_OUT_BF16) >= 0
     assert lib.fp8_block_gemm_workspace_bytes(4, 4, 100, L.FP8Q_OUT_BF16) == 0
     assert lib.fp8_block_gemm_workspace_bytes(4, 4, 128, 9) == 0
+    # the K-block-major scale flag: its own size limit; unknown flag bits are rejected; the
+    # workspace does not depend on the scale layout
+    km = L.FP8Q_OUT_BF16 | L.FP8Q_SA_KMAJOR
+    assert call(dt=km, M=1 << 23, K=64 * 128) == L.FP8Q_ERR_SHAPE
+    assert call(dt=km | L.FP8Q_GEMM_EXACT_SLICES, M=1 << 23, K=64 * 128) == L.FP8Q_ERR_SHAPE
+    assert call(dt=L.FP8Q_OUT_BF16 | 0x2000) == L.FP8Q_ERR_DTYPE
+    assert call(dt=km, sa=FAKE + 2) == L.FP8Q_ERR_ALIGN
+    assert call(dt=km, M=0, aq=None, sa=None, wq=None, sw=None, y=None) == L.FP8Q_OK
+    for shape in ((4096, 576, 7168), (128, 7168, 7168), (4096, 1536, 7168)):
+        assert (lib.fp8_block_gemm_workspace_bytes(*shape, km) ==
+                lib.fp8_block_gemm_workspace_bytes(*shape, L.FP8Q_OUT_BF16))
 
 
 def test_python_binding_rejects_cpu_tensors_and_bad_shapes():
@@ -147,6 +174,7 @@ def test_grouped_and_training_validation(lib):
     assert g(FAKE, FAKE, FAKE, FAKE, FAKE + 4, FAKE, 0, 2, 4, 8, 128, None) == L.FP8Q_ERR_ALIGN
     assert g(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 5, 2, 4, 8, 128, None) == L.FP8Q_ERR_DTYPE
     assert g(None, None, None, None, None, None, 0, 2, 0, 8, 128, None) == L.FP8Q_OK              # no rows
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 | L.FP8Q_SA_KMAJOR, 2, 4, 8, 128, None) == L.FP8Q_ERR_DTYPE
     t = lib.fp8_act_quant_t
     assert t(FAKE, FAKE, FAKE, 4, 12, None) == L.FP8Q_ERR_SHAPE                                    # C % 8
     assert t(FAKE, FAKE, FAKE, -1, 16, None) == L.FP8Q_ERR_SHAPE
@@ -159,6 +187,7 @@ def test_grouped_and_training_validation(lib):
     assert wt(FAKE, None, FAKE, FAKE, 16, 128, None) == L.FP8Q_ERR_NULL
     r = lib.fp8_rowwise_gemm
     assert r(FAKE, FAKE, FAKE, FAKE, FAKE, 9, 4, 4, 128, None, 0, None) == L.FP8Q_ERR_DTYPE
+    assert r(FAKE, FAKE, FAKE, FAKE, FAKE, 1 | L.FP8Q_SA_KMAJOR, 4, 4, 128, None, 0, None) == L.FP8Q_ERR_DTYPE
     assert r(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 4, 4, 100, None, 0, None) == L.FP8Q_ERR_SHAPE
     assert r(FAKE, FAKE, FAKE, FAKE, None, 0, 4, 4, 128, None, 0, None) == L.FP8Q_ERR_NULL
     assert r(FAKE, FAKE, FAKE + 8, FAKE, FAKE, 0, 4, 4, 128, None, 0, None) == L.FP8Q_ERR_ALIGN

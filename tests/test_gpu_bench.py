@@ -37,3 +37,4 @@ def test_bench_json_contract():
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["cores"] >= 1 and cb["value"] > 0 and cb["sample"]
     assert cb["gpu_codes_match_oracle_on_sample"] is True
+    assert cb["gpu_scales_match_oracle_on_sample"] is True

@@ -327,6 +327,76 @@ def test_gemm_every_tile_every_slice_count(nkb):
         fq.lib.fp8q_gemm_force_config(-1, 0)
 
 
+@pytest.mark.parametrize("M,N,K", [(300, 576, 2048), (129, 200, 1280), (1000, 300, 7168), (37, 64, 384)])
+def test_gemm_kmajor_scales_every_tile(M, N, K):
+    """K-block-major activation scales (FP8Q_SA_KMAJOR). In the default configuration the
+    output meets the bound against the oracle in both modes; every tile configuration,
+    with and without split-K, gives output bit-identical to the row-major scales' (the
+    scale values and every arithmetic step are the same, only where the copies read them
+    differs). With ragged M the last tile's rows past M read other slices' scales in this
+    layout; they feed only outputs that are never stored."""
+    from fp8_act_quant_amd import _lib as L
+    A = synth.random_bf16((M, K), seed=31 * M + K)
+    W = synth.random_bf16((N, K), seed=37 * N + K, std=0.02)
+    aq, sa, wq, sw = quantise_on_gpu(A, W)
+    aqk, sak = fq.act_quant(dev_bf16(A), scale_layout="kmajor")
+    assert torch.equal(aq.view(torch.uint8), aqk.view(torch.uint8))
+    assert torch.equal(sa.view(torch.int32), sak.contiguous().view(torch.int32))
+    haq, hsa, hwq, hsw = host_codes(aq), sa.cpu().numpy(), host_codes(wq), sw.cpu().numpy()
+    y_hat, bound = oracle.block_gemm(haq, hsa, hwq, hsw)
+    rows, cols = np.repeat(np.arange(M), N), np.tile(np.arange(N), M)
+    floor = scale_floor(haq, hwq, rows, cols).reshape(M, N)
+    fp8_allow = floor + mfma_group_allowance(haq, hsa, hwq, hsw, rows, cols).reshape(M, N)
+    for out, mode in (("bf16", "fp8"), ("f32", "exact")):
+        y = fq.fp8_gemm(aqk, sak, wq, sw, out_dtype=TORCH_OUT[out], mode=mode)
+        torch.cuda.synchronize()
+        res = gemm_check(y_host(y, out), y_hat, bound, out, fp8_allow if mode == "fp8" else floor)
+        print(f"kmajor {M}x{N}x{K} {out} {mode}", res, flush=True)
+        assert res["violations"] == 0, (out, mode, res)
+    ws = torch.zeros(64 << 20, dtype=torch.uint8, device="cuda")
+    bits = {"bf16": torch.int16, "f32": torch.int32}
+    try:
+        for c, name in enumerate(_configs()):
+            for splits in (1, 2):
+                assert fq.lib.fp8q_gemm_force_config(c, splits) == L.FP8Q_OK
+                for out, mode in (("bf16", "fp8"), ("f32", "fp8"), ("f32", "exact")):
+                    if splits > 1 and mode == "exact":
+                        continue
+                    yr = fq.fp8_gemm(aq, sa, wq, sw, out_dtype=TORCH_OUT[out], mode=mode, workspace=ws)
+                    yk = fq.fp8_gemm(aqk, sak, wq, sw, out_dtype=TORCH_OUT[out], mode=mode, workspace=ws)
+                    torch.cuda.synchronize()
+                    assert torch.equal(yr.view(bits[out]), yk.view(bits[out])), (name, splits, out, mode)
+    finally:
+        fq.lib.fp8q_gemm_force_config(-1, 0)
+
+
+def test_gemm_kmajor_scales_bias_and_errors():
+    """The bias epilogue with K-block-major scales; scale tensors in neither layout, and
+    the grouped GEMM given the flag, are rejected."""
+    from fp8_act_quant_amd import _lib as L
+    M, N, K = 260, 576, 1024
+    A = synth.random_bf16((M, K), seed=61)
+    W = synth.random_bf16((N, K), seed=62, std=0.02)
+    aq, sa, wq, sw = quantise_on_gpu(A, W)
+    aqk, sak = fq.act_quant(dev_bf16(A), scale_layout="kmajor")
+    b = dev_f32(np.random.Generator(np.random.PCG64(63)).standard_normal(N).astype(np.float32))
+    for out in ("bf16", "f32"):
+        yr = fq.fp8_gemm(aq, sa, wq, sw, out_dtype=TORCH_OUT[out], mode="fp8", bias=b)
+        yk = fq.fp8_gemm(aqk, sak, wq, sw, out_dtype=TORCH_OUT[out], mode="fp8", bias=b)
+        torch.cuda.synchronize()
+        assert torch.equal(yr.view(torch.int16 if out == "bf16" else torch.int32),
+                           yk.view(torch.int16 if out == "bf16" else torch.int32))
+    with pytest.raises(ValueError):
+        fq.fp8_gemm(aq, torch.empty((M, 2 * (K // 128)), device="cuda")[:, ::2], wq, sw)
+    with pytest.raises(ValueError):
+        fq.fp8_gemm(aq, torch.empty((K // 128 * 2, M), device="cuda")[::2].t(), wq, sw)
+    offs = torch.tensor([0, M], dtype=torch.int64, device="cuda")
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    assert fq.lib.fp8_grouped_gemm(aqk.data_ptr(), sak.data_ptr(), wq.data_ptr(), sw.data_ptr(), offs.data_ptr(),
+                                   y.data_ptr(), L.FP8Q_OUT_BF16 | L.FP8Q_SA_KMAJOR, 1, M, N, K,
+                                   None) == L.FP8Q_ERR_DTYPE
+
+
 def test_linear_dispatch():
     """linear(): the FP8 branch is act_quant + fp8_gemm with the bias fused; the bf16
     branch dequantises the weight and applies torch's linear; a bf16 weight is used as is."""
@@ -355,9 +425,12 @@ def test_gemm_workload_full_size_sampled(name):
     wl = synth.WORKLOADS[name]
     A, W = synth.make_inputs(wl)
     print(f"gemm parity {name} M={wl.M} N={wl.N} K={wl.K} out={wl.out_dtype}", flush=True)
-    aq, sa, wq, sw = quantise_on_gpu(A, W)
-    y = fq.fp8_gemm(aq, sa, wq, sw, out_dtype=TORCH_OUT[wl.out_dtype])
+    # the benchmark's launch: K-block-major activation scales
+    aq, sak = fq.act_quant(dev_bf16(A), scale_layout="kmajor")
+    wq, sw = fq.weight_quant(dev_bf16(W))
+    y = fq.fp8_gemm(aq, sak, wq, sw, out_dtype=TORCH_OUT[wl.out_dtype])
     torch.cuda.synchronize()
+    sa = sak.contiguous()
     rows, cols = synth.sample_outputs(wl.M, wl.N, 8192, seed=1)
     haq, hsa, hwq, hsw = host_codes(aq), sa.cpu().numpy(), host_codes(wq), sw.cpu().numpy()
     # the codes the GEMM consumed are the oracle's codes (quantiser parity)

@@ -104,6 +104,62 @@ def test_act_quant_workload_full_size(name):
     assert_act_parity(A, name)
 
 
+# nkb = K/128 from 1 to 129 (powers of two and their neighbours, odd counts), ragged M
+@pytest.mark.parametrize("M,K", [(1, 128), (3, 256), (37, 384), (5, 640), (257, 7168), (1000, 128 * 57),
+                                 (64, 128 * 63), (33, 128 * 64), (17, 128 * 65), (9, 128 * 129)])
+def test_act_quant_kmajor_small_shapes(M, K):
+    """fp8_act_quant_kmajor: the oracle's codes, and its scale grid transposed, bit for bit."""
+    A = synth.random_bf16((M, K), seed=M * 13 + K)
+    q, s = fq.act_quant(dev_bf16(A), scale_layout="kmajor")
+    torch.cuda.synchronize()
+    assert s.shape == (M, K // 128) and s.movedim(-1, 0).is_contiguous()
+    oq, os_ = oracle.act_quant(A)
+    assert np.array_equal(host_codes(q), oq), f"{M}x{K}: codes differ"
+    st = host_f32_bits(s.movedim(-1, 0))
+    assert np.array_equal(st, np.ascontiguousarray(os_.T).view(np.uint32)), f"{M}x{K}: scales differ"
+
+
+def test_act_quant_kmajor_leading_dims_and_empty():
+    A = synth.random_bf16((2, 3, 512), seed=4)
+    q, s = fq.act_quant(dev_bf16(A), scale_layout="kmajor")
+    torch.cuda.synchronize()
+    oq, os_ = oracle.act_quant(A.reshape(6, 512))
+    assert q.shape == (2, 3, 512) and s.shape == (2, 3, 4)
+    assert np.array_equal(host_codes(q).reshape(6, 512), oq)
+    assert np.array_equal(host_f32_bits(s.contiguous()).reshape(6, 4), os_.view(np.uint32))
+    q, s = fq.act_quant(torch.empty((0, 256), dtype=torch.bfloat16, device="cuda"), scale_layout="kmajor")
+    assert q.shape == (0, 256) and s.shape == (0, 2)
+    with pytest.raises(ValueError):
+        fq.act_quant(dev_bf16(A), scale_layout="col")
+
+
+def test_act_quant_kmajor_workload_full_size():
+    """The benchmark's act_quant (query down-projection activations) in the K-block-major
+    layout it runs with, against the oracle."""
+    A, _ = synth.make_inputs("q_down", with_weight=False)
+    q, s = fq.act_quant(dev_bf16(A), scale_layout="kmajor")
+    torch.cuda.synchronize()
+    oq, os_ = oracle.act_quant(A)
+    assert np.array_equal(host_codes(q), oq)
+    assert np.array_equal(host_f32_bits(s.movedim(-1, 0)), np.ascontiguousarray(os_.T).view(np.uint32))
+
+
+def test_act_quant_kmajor_large_tile_index():
+    """About 2^24 tiles (K/128 = 57): the tile -> (row, K slice) division at large tile
+    numbers, against the row-major kernel on the same input (bit-exact against the oracle
+    above): equal codes, and scales that are the transpose of each other."""
+    M, K = 300007, 128 * 57
+    print(f"act_quant kmajor vs row-major {M}x{K}", flush=True)
+    g = torch.Generator(device="cuda").manual_seed(11)
+    x = torch.randn((M, K), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    qr, sr = fq.act_quant(x)
+    qk, sk = fq.act_quant(x, scale_layout="kmajor")
+    torch.cuda.synchronize()
+    assert torch.equal(qr.view(torch.uint8), qk.view(torch.uint8))
+    assert torch.equal(sr.view(torch.int32), sk.contiguous().view(torch.int32))
+    del x, qr, qk
+
+
 @pytest.mark.slow
 @pytest.mark.timeout(900)
 def test_act_quant_exhaustive_bf16_pairs():
