@@ -370,6 +370,27 @@ def test_gemm_kmajor_scales_every_tile(M, N, K):
         fq.lib.fp8q_gemm_force_config(-1, 0)
 
 
+def test_gemm_kmajor_scales_large_m():
+    """300007 rows, K/128 = 57: per-slice scale offsets of kb * M * 4 bytes up to 68 MB and
+    a ragged last tile. Output bit-identical to the row-major scales' (whose kernel path is
+    checked against the oracle above), in both modes."""
+    M, N, K = 300007, 256, 128 * 57
+    print(f"gemm kmajor vs row-major {M}x{N}x{K}", flush=True)
+    g = torch.Generator(device="cuda").manual_seed(12)
+    x = torch.randn((M, K), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    w = (0.02 * torch.randn((N, K), generator=g, device="cuda", dtype=torch.float32)).to(torch.bfloat16)
+    aq, sa = fq.act_quant(x)
+    aqk, sak = fq.act_quant(x, scale_layout="kmajor")
+    del x
+    wq, sw = fq.weight_quant(w)
+    for out, mode, bits in (("bf16", "fp8", torch.int16), ("f32", "exact", torch.int32)):
+        yr = fq.fp8_gemm(aq, sa, wq, sw, out_dtype=TORCH_OUT[out], mode=mode)
+        yk = fq.fp8_gemm(aqk, sak, wq, sw, out_dtype=TORCH_OUT[out], mode=mode)
+        torch.cuda.synchronize()
+        assert torch.equal(yr.view(bits), yk.view(bits)), (out, mode)
+        del yr, yk
+
+
 def test_gemm_kmajor_scales_bias_and_errors():
     """The bias epilogue with K-block-major scales; scale tensors in neither layout, and
     the grouped GEMM given the flag, are rejected."""
