@@ -34,6 +34,11 @@ FP8_PEAK_TFLOPS = 5000.0      # MI355X dense FP8 MFMA
 HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
 METRIC = "fp8_block_gemm TFLOP/s (incl. act_quant) and % of MI355X FP8 MFMA peak"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_q_down_traffic.json")
+MFMA_FILE = os.path.join(ROOT, "profiles", "gemm_q_down_mfma_busy.json")
+# MI355X: GRBM_GUI_ACTIVE is reported once per XCD (8) and summed; SQ_VALU_MFMA_BUSY_CYCLES is
+# summed over every SIMD (256 CUs x 4), so busy / (GUI_ACTIVE / XCDS * SIMDS) is the fraction of
+# the kernel's cycles in which the average SIMD's matrix unit was busy (rocprofv3's MfmaUtil)
+XCDS, SIMDS = 8, 1024
 GEMM_SOURCES = ["fp8_act_quant_amd/csrc/gemm.hip", "fp8_act_quant_amd/csrc/device_common.h"]
 
 
@@ -97,17 +102,48 @@ def kernel_source_sha() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per GEMM launch from the committed counter summary, if it was taken on
-    the current kernel source; otherwise None."""
+def _stored(path: str, key: str):
+    """A figure from a committed counter summary, if it was taken on the current GEMM source."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
     if t.get("kernel_source_sha") != kernel_source_sha():
         return None
-    return t.get("hbm_bytes_per_launch")
+    return t.get(key)
+
+
+def measured_mfma_busy():
+    """The GEMM's matrix-unit busy fraction from the committed counter summary, or None."""
+    return _stored(MFMA_FILE, "mfma_busy_frac")
+
+
+def write_mfma_summary(csv_path: str) -> dict:
+    """Matrix-unit busy fraction of the q_down GEMM from one rocprofv3 --pmc run with
+    SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE, stored with the kernel source hash."""
+    busy = _per_dispatch(csv_path, "SQ_VALU_MFMA_BUSY_CYCLES")["gemm"]
+    active = _per_dispatch(csv_path, "GRBM_GUI_ACTIVE")["gemm"]
+    cycles = active / XCDS
+    summary = {
+        "kernel_source_sha": kernel_source_sha(),
+        "workload": "q_down 4096x1536x7168 bf16 out",
+        "sq_valu_mfma_busy_cycles_per_dispatch": round(busy, 1),
+        "grbm_gui_active_per_dispatch": round(active, 1),
+        "xcds": XCDS,
+        "simds": SIMDS,
+        "kernel_cycles": round(cycles, 1),
+        "mfma_busy_frac": round(busy / (cycles * SIMDS), 4),
+    }
+    with open(MFMA_FILE, "w") as f:
+        json.dump(summary, f, indent=1)
+    return summary
+
+
+def measured_traffic():
+    """HBM bytes per GEMM launch from the committed counter summary, if it was taken on
+    the current kernel source; otherwise None."""
+    return _stored(TRAFFIC_FILE, "hbm_bytes_per_launch")
 
 
 COPY_BYTES = 256 << 20   # bytes read (and written) by the calibration copy
@@ -315,10 +351,16 @@ def main() -> int:
                          "skips the routed-expert measurement")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the GEMM's HBM traffic summary from two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--mfma-from", metavar="PMC_CSV",
+                    help="write the GEMM's matrix-unit busy summary from a rocprofv3 --pmc run of "
+                         "SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE and exit")
     args = ap.parse_args()
 
     if args.traffic_from:
         print(json.dumps(write_traffic_summary(*args.traffic_from)), flush=True)
+        return 0
+    if args.mfma_from:
+        print(json.dumps(write_mfma_summary(args.mfma_from)), flush=True)
         return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -436,6 +478,8 @@ def main() -> int:
             "unit": "TFLOP/s",
             "frac": round(gemm_tflops / FP8_PEAK_TFLOPS, 4),
             "traffic": traffic,
+            # rocprof MFMA-busy counters (matrix unit busy over the kernel's cycles at its own clock)
+            "mfma_busy_frac": measured_mfma_busy(),
             "avg_launch_us": round(float(t_gemm.mean()) * 1e6, 3),
             "algorithmic_flops_per_launch": flops,
         },

@@ -66,3 +66,32 @@ def test_more_than_one_gpu_is_refused():
                        text=True, timeout=300)
     assert r.returncode != 0
     assert "--gpus must be 1" in r.stderr
+
+
+def test_mfma_busy_summary(tmp_path, monkeypatch):
+    """MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / XCDs * SIMDs), per GEMM
+    dispatch (rocprofv3's MfmaUtil); other kernels are ignored; the stored figure is used only
+    while the kernel source is unchanged."""
+    p = tmp_path / "m.csv"
+    with open(p, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        for d, busy, gui in ((1, 512000.0, 8000.0), (2, 256000.0, 8000.0)):
+            # eight XCD instances of the GUI counter, busy split over two SE rows
+            for _ in range(8):
+                w.writerow({"Dispatch_Id": d, "Kernel_Name": GEMM, "Counter_Name": "GRBM_GUI_ACTIVE",
+                            "Counter_Value": gui / 8})
+            for _ in range(2):
+                w.writerow({"Dispatch_Id": d, "Kernel_Name": GEMM, "Counter_Name": "SQ_VALU_MFMA_BUSY_CYCLES",
+                            "Counter_Value": busy / 2})
+        w.writerow({"Dispatch_Id": 3, "Kernel_Name": AQ, "Counter_Name": "SQ_VALU_MFMA_BUSY_CYCLES",
+                    "Counter_Value": 1e12})
+    out = tmp_path / "mfma.json"
+    monkeypatch.setattr(bench, "MFMA_FILE", str(out))
+    s = bench.write_mfma_summary(str(p))
+    # mean busy 384000 over 1000 cycles x 1024 SIMDs
+    assert s["kernel_cycles"] == pytest.approx(1000.0)
+    assert s["mfma_busy_frac"] == pytest.approx(384000.0 / (1000.0 * 1024), abs=1e-4)
+    assert bench.measured_mfma_busy() == s["mfma_busy_frac"]
+    monkeypatch.setattr(bench, "kernel_source_sha", lambda: "f" * 16)
+    assert bench.measured_mfma_busy() is None

@@ -34,6 +34,7 @@ def test_bench_json_contract():
     assert rf["achieved"] == pytest.approx(rf["algorithmic_flops_per_launch"] / (rf["avg_launch_us"] * 1e-6) / 1e12,
                                            rel=1e-3)
     assert rf["traffic"] is None or rf["traffic"] > 0
+    assert rf["mfma_busy_frac"] is None or 0 < rf["mfma_busy_frac"] < 1
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["cores"] >= 1 and cb["value"] > 0 and cb["sample"]
     assert cb["gpu_codes_match_oracle_on_sample"] is True
