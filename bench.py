@@ -364,8 +364,8 @@ def main() -> int:
         return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the path is data-parallel over tokens with no exchange, "
-              "and this build runs on a single MI355X; --gpus must be 1.", file=sys.stderr)
+        print("bench.py measures one MI355X: the path is data-parallel over tokens with no exchange "
+              "between GPUs, so a multi-GPU figure is N times this one; --gpus must be 1.", file=sys.stderr)
         return 2
 
     import numpy as np
