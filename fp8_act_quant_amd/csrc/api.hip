@@ -16,8 +16,11 @@ constexpr int kMaxDevices = 64;
 // launch-geometry limits of the kernels (grid dimensions are 32-bit)
 constexpr int64_t kMaxElems = (int64_t)1 << 46;
 constexpr int64_t kMaxWeightBlockRows = 65535;
-// the GEMM addresses a workgroup's rows of A and W with 32-bit offsets: K <= 2^24
-constexpr int64_t kMaxGemmK = (int64_t)1 << 24;
+// The GEMM addresses a workgroup's rows of A and W (at most 256 rows of K bytes) through
+// buffer resources whose byte count is 32-bit and which read zero past it: 256 * K must stay
+// below 2^32, so K < 2^24 (a count of exactly 2^32 cannot be stated, and its last bytes would
+// read as zero).
+constexpr int64_t kMaxGemmK = ((int64_t)1 << 24) - 128;
 // grid dimensions of the two-dimensional launches
 constexpr int64_t kMaxGridX = 0x7FFFFFFF, kMaxGridY = 65535;
 // K-block-major activation scales are addressed with 32-bit byte offsets: M * K/128 < 2^29

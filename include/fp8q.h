@@ -135,7 +135,7 @@ int fp8_weight_dequant(const uint8_t *q, const float *s, uint16_t *w, int64_t N,
  *   y  [M, N] output, fp32 (y_dtype = FP8Q_OUT_F32) or bf16 bits (FP8Q_OUT_BF16, RNE of
  *      the fp32 accumulator). With K = 0 the output is all zeros.
  *   aq, wq, y: 16-byte aligned; sa, sw: 4-byte aligned. M, N >= 0 arbitrary (ragged tails
- *   are masked), K a multiple of 128 and at most 2^24.
+ *   are masked), K a multiple of 128 and below 2^24 (at most 2^24 - 128).
  *   workspace / workspace_bytes: optional device scratch (16-byte aligned) for a split-K
  *   schedule, used by shapes with too few output tiles to fill the GPU; pass NULL / 0 to run
  *   without it. If workspace_bytes is smaller than fp8_block_gemm_workspace_bytes() the call

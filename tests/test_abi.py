@@ -134,6 +134,9 @@ def test_block_gemm_validation(lib):
     assert call(M=0, aq=None, sa=None, wq=None, sw=None, y=None) == L.FP8Q_OK
     assert call(N=0, aq=None, sa=None, wq=None, sw=None, y=None) == L.FP8Q_OK
     assert call(M=1 << 30, N=1 << 30) == L.FP8Q_ERR_SHAPE
+    # K below 2^24: a 256-row tile's byte range (256 K) must be stated in 32 bits
+    assert call(K=1 << 24) == L.FP8Q_ERR_SHAPE
+    assert lib.fp8_block_gemm_workspace_bytes(4, 4, 1 << 24, L.FP8Q_OUT_BF16) == 0
     assert lib.fp8_block_gemm_workspace_bytes(4096, 576, 7168, L.FP8Q_OUT_BF16) >= 0
     assert lib.fp8_block_gemm_workspace_bytes(4, 4, 100, L.FP8Q_OUT_BF16) == 0
     assert lib.fp8_block_gemm_workspace_bytes(4, 4, 128, 9) == 0

@@ -370,6 +370,46 @@ def test_gemm_kmajor_scales_every_tile(M, N, K):
         fq.lib.fp8q_gemm_force_config(-1, 0)
 
 
+def test_gemm_maximum_k():
+    """The largest K the ABI takes (2^24 - 128, 131071 slices) with 256-row tiles, whose
+    row offsets into A reach 255 * K + K - 16, just below 2^32: forced 256x128 (exact slices,
+    fp32 out, and FP8 products, bf16 out) and 256x256 (FP8 products), plus the planner's choice
+    with a split-K workspace, each against the oracle on sampled outputs that include the last
+    row of the 256-row tile and the ragged last column. (The K limit itself: test_abi.)"""
+    from fp8_act_quant_amd import _lib as L
+    M, N, K = 256, 200, (1 << 24) - 128
+    print(f"gemm maximum K {M}x{N}x{K}", flush=True)
+    g = torch.Generator(device="cuda").manual_seed(14)
+    x = torch.randn((M, K), generator=g, device="cuda", dtype=torch.bfloat16)
+    aq, sa = fq.act_quant(x)
+    del x
+    w = torch.randn((N, K), generator=g, device="cuda", dtype=torch.bfloat16) * 0.02
+    wq, sw = fq.weight_quant(w)
+    del w
+    torch.cuda.synchronize()
+    haq, hsa, hwq, hsw = host_codes(aq), sa.cpu().numpy(), host_codes(wq), sw.cpu().numpy()
+    rng = np.random.Generator(np.random.PCG64(15))
+    rows = np.concatenate([[0, 127, 128, 255, 255, 255], rng.integers(0, M, 10)]).astype(np.int64)
+    cols = np.concatenate([[0, 199, 128, 0, 127, 199], rng.integers(0, N, 10)]).astype(np.int64)
+    y_hat, bound = oracle.block_gemm_sampled(haq, hsa, hwq, hsw, rows, cols)
+    floor = scale_floor(haq, hwq, rows, cols, chunk=4)
+    fp8_allow = floor + mfma_group_allowance(haq, hsa, hwq, hsw, rows, cols, chunk=4)
+    names = _configs()
+    ws = torch.zeros(64 << 20, dtype=torch.uint8, device="cuda")
+    cases = [("256x128w8", "f32", "exact"), ("256x128w8", "bf16", "fp8"), ("256x256w8", "bf16", "fp8"),
+             (None, "bf16", "fp8"), (None, "f32", "exact")]
+    try:
+        for name, out, mode in cases:
+            assert fq.lib.fp8q_gemm_force_config(names.index(name) if name else -1, 1 if name else 0) == L.FP8Q_OK
+            y = fq.fp8_gemm(aq, sa, wq, sw, out_dtype=TORCH_OUT[out], mode=mode, workspace=None if name else ws)
+            torch.cuda.synchronize()
+            res = gemm_check(y_host(y, out)[rows, cols], y_hat, bound, out, fp8_allow if mode == "fp8" else floor)
+            print(f"maximum K {name or 'planner'} {out} {mode}", res, flush=True)
+            assert res["violations"] == 0, (name, out, mode, res)
+    finally:
+        fq.lib.fp8q_gemm_force_config(-1, 0)
+
+
 def test_gemm_kmajor_scales_large_m():
     """300007 rows, K/128 = 57: per-slice scale offsets of kb * M * 4 bytes up to 68 MB and
     a ragged last tile. Output bit-identical to the row-major scales' (whose kernel path is
