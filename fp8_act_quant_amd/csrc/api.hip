@@ -23,6 +23,8 @@ constexpr int64_t kMaxWeightBlockRows = 65535;
 constexpr int64_t kMaxGemmK = ((int64_t)1 << 24) - 128;
 // grid dimensions of the two-dimensional launches
 constexpr int64_t kMaxGridX = 0x7FFFFFFF, kMaxGridY = 65535;
+// a grid dimension counts at most 2^32 - 1 work-items: workgroups of 256 threads along it
+constexpr int64_t kMaxBlocks256 = 0xFFFFFFFFll / 256;
 // K-block-major activation scales are addressed with 32-bit byte offsets: M * K/128 < 2^29
 constexpr int64_t kMaxKmajorScales = (int64_t)1 << 29;
 
@@ -80,6 +82,7 @@ int fp8_act_quant_kmajor(const uint16_t *x, uint8_t *q, float *s, int64_t M, int
 int fp8_weight_quant(const uint16_t *w, uint8_t *q, float *s, int64_t N, int64_t K, void *stream) {
     if (int e = shape_ok(N, K)) return e;
     if ((N + kBlock - 1) / kBlock > kMaxWeightBlockRows) return FP8Q_ERR_SHAPE;
+    if (K / kBlock > kMaxBlocks256) return FP8Q_ERR_SHAPE;   // one workgroup per 128-column block
     if (N == 0 || K == 0) return FP8Q_OK;
     if (!w || !q || !s) return FP8Q_ERR_NULL;
     if (misaligned(w, 16) || misaligned(q, 16) || misaligned(s, 4)) return FP8Q_ERR_ALIGN;
@@ -158,7 +161,7 @@ int fp8_grouped_gemm(const uint8_t *aq, const float *sa, const uint8_t *wq, cons
 int fp8_act_quant_t(const uint16_t *x, uint8_t *qt, float *st, int64_t M, int64_t C, void *stream) {
     if (M < 0 || C < 0 || (C % 8) != 0) return FP8Q_ERR_SHAPE;
     const int64_t ldq = (M + kBlock - 1) / kBlock * kBlock;
-    if ((C > 0 && ldq > kMaxElems / C) || (C + 127) / 128 > kMaxGridY || ldq / kBlock > kMaxGridX) return FP8Q_ERR_SHAPE;
+    if ((C > 0 && ldq > kMaxElems / C) || (C + 127) / 128 > kMaxGridY || ldq / kBlock > kMaxBlocks256) return FP8Q_ERR_SHAPE;
     if (M == 0 || C == 0) return FP8Q_OK;
     if (!x || !qt || !st) return FP8Q_ERR_NULL;
     if (misaligned(x, 16) || misaligned(qt, 16) || misaligned(st, 4)) return FP8Q_ERR_ALIGN;
@@ -169,7 +172,7 @@ int fp8_act_quant_t(const uint16_t *x, uint8_t *qt, float *st, int64_t M, int64_
 int fp8_weight_transpose(const uint8_t *wq, const float *sw, uint8_t *wqt, float *swt, int64_t N, int64_t K,
                          void *stream) {
     if (int e = shape_ok(N, K)) return e;
-    if ((N + 63) / 64 > kMaxGridY) return FP8Q_ERR_SHAPE;
+    if ((N + 63) / 64 > kMaxGridY || K / 64 > kMaxBlocks256) return FP8Q_ERR_SHAPE;   // 64x64-byte tiles
     if (N == 0 || K == 0) return FP8Q_OK;
     if (!wq || !sw || !wqt || !swt) return FP8Q_ERR_NULL;
     if (misaligned(wq, 16) || misaligned(wqt, 16) || misaligned(sw, 4) || misaligned(swt, 4)) return FP8Q_ERR_ALIGN;

@@ -1127,7 +1127,10 @@ static hipError_t launch_cfg(GemmArgs a, bool out_bf16, int splits, hipStream_t 
     a.tiles_n = (int)((a.N + BN - 1) / BN);
     a.group = choose_group(a.tiles_m, a.tiles_n, BM, BN);
     a.splits = splits;
-    const dim3 grid((unsigned)((int64_t)a.tiles_m * a.tiles_n * splits)), block(NW * 64);
+    // a grid dimension counts at most 2^32 - 1 work-items
+    const int64_t units = (int64_t)a.tiles_m * a.tiles_n * splits;
+    if (units * NW * 64 > 0xFFFFFFFFll) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)units), block(NW * 64);
     if (out_bf16)
         block_gemm_kernel<BM, BN, NW, WAVES_M, NSTAGE, 1, EXACT, GROUPED, ROWB><<<grid, block, 0, stream>>>(a);
     else

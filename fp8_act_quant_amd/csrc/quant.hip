@@ -232,9 +232,10 @@ hipError_t launch_weight_quant(const uint16_t *w, uint8_t *q, float *s, int64_t 
 }
 
 // ------------------------------------------------------------------------------------
-// weight_dequant: each thread turns one 16-byte chunk of codes (16 consecutive k inside
-// one 128-wide block) into 16 bf16 values: decode (v_cvt_pk_f32_fp8), one fp32 multiply
-// by the block scale, round to bf16 (v_cvt_pk_bf16_f32).
+// weight_dequant: each thread turns 16-byte chunks of codes (16 consecutive k inside one
+// 128-wide block) into 16 bf16 values: decode (v_cvt_pk_f32_fp8), one fp32 multiply by the
+// block scale, round to bf16 (v_cvt_pk_bf16_f32). Grid-stride over the chunks, so the
+// launch stays within the 32-bit work-item count of a grid dimension at any size.
 // ------------------------------------------------------------------------------------
 constexpr int DQ_THREADS = 256;
 
@@ -248,31 +249,35 @@ __global__ __launch_bounds__(DQ_THREADS) void weight_dequant_kernel(const u32x4 
                                                                     const float *__restrict__ s,
                                                                     u32x4 *__restrict__ w,
                                                                     int64_t n_chunks, int64_t K) {
-    const int64_t c = (int64_t)blockIdx.x * DQ_THREADS + threadIdx.x;
-    if (c >= n_chunks) return;
     const int64_t chunks_per_row = K / 16;
-    const int64_t n = c / chunks_per_row;
-    const int64_t k = (c - n * chunks_per_row) * 16;
-    const float sc = s[(n / kBlock) * (K / kBlock) + k / kBlock];
-    const u32x4 v = __builtin_nontemporal_load(&q[c]);
-    u32x4 o0, o1;
-    o0.x = dequant_pair<false>(v.x, sc);
-    o0.y = dequant_pair<true>(v.x, sc);
-    o0.z = dequant_pair<false>(v.y, sc);
-    o0.w = dequant_pair<true>(v.y, sc);
-    o1.x = dequant_pair<false>(v.z, sc);
-    o1.y = dequant_pair<true>(v.z, sc);
-    o1.z = dequant_pair<false>(v.w, sc);
-    o1.w = dequant_pair<true>(v.w, sc);
-    __builtin_nontemporal_store(o0, &w[2 * c]);
-    __builtin_nontemporal_store(o1, &w[2 * c + 1]);
+    for (int64_t c = (int64_t)blockIdx.x * DQ_THREADS + threadIdx.x; c < n_chunks;
+         c += (int64_t)gridDim.x * DQ_THREADS) {
+        const int64_t n = c / chunks_per_row;
+        const int64_t k = (c - n * chunks_per_row) * 16;
+        const float sc = s[(n / kBlock) * (K / kBlock) + k / kBlock];
+        const u32x4 v = __builtin_nontemporal_load(&q[c]);
+        u32x4 o0, o1;
+        o0.x = dequant_pair<false>(v.x, sc);
+        o0.y = dequant_pair<true>(v.x, sc);
+        o0.z = dequant_pair<false>(v.y, sc);
+        o0.w = dequant_pair<true>(v.y, sc);
+        o1.x = dequant_pair<false>(v.z, sc);
+        o1.y = dequant_pair<true>(v.z, sc);
+        o1.z = dequant_pair<false>(v.w, sc);
+        o1.w = dequant_pair<true>(v.w, sc);
+        __builtin_nontemporal_store(o0, &w[2 * c]);
+        __builtin_nontemporal_store(o1, &w[2 * c + 1]);
+    }
 }
 
 hipError_t launch_weight_dequant(const uint8_t *q, const float *s, uint16_t *w, int64_t N, int64_t K,
                                  hipStream_t stream) {
     const int64_t n_chunks = N * (K / 16);
     if (n_chunks == 0) return hipSuccess;
-    const int64_t blocks = (n_chunks + DQ_THREADS - 1) / DQ_THREADS;
+    // 64 workgroups per CU, then grid-stride (an offline kernel: the loop costs nothing measurable)
+    const int64_t cap = (int64_t)256 * 64;
+    const int64_t want = (n_chunks + DQ_THREADS - 1) / DQ_THREADS;
+    const int64_t blocks = want < cap ? want : cap;
     hipLaunchKernelGGL(weight_dequant_kernel, dim3((unsigned)blocks), dim3(DQ_THREADS), 0, stream,
                        reinterpret_cast<const u32x4 *>(q), s, reinterpret_cast<u32x4 *>(w), n_chunks, K);
     return hipGetLastError();

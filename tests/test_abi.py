@@ -102,6 +102,9 @@ def test_weight_quant_and_dequant_validation(lib):
         assert fn(FAKE, FAKE + 1, FAKE, 4, 128, None) == L.FP8Q_ERR_ALIGN
         assert fn(None, None, None, 0, 256, None) == L.FP8Q_OK
         assert fn(FAKE, FAKE, FAKE, 128 * 65536, 128, None) == L.FP8Q_ERR_SHAPE
+        # a grid dimension counts at most 2^32 - 1 work-items (one 256-thread workgroup per
+        # 128-column block)
+        assert fn(FAKE, FAKE, FAKE, 1, 1 << 31, None) == L.FP8Q_ERR_SHAPE
     assert lib.fp8_weight_dequant(FAKE, FAKE, FAKE, 4, 64, None) == L.FP8Q_ERR_SHAPE
     assert lib.fp8_weight_dequant(FAKE, None, FAKE, 4, 128, None) == L.FP8Q_ERR_NULL
     assert lib.fp8_weight_dequant(FAKE, FAKE, FAKE + 2, 4, 128, None) == L.FP8Q_ERR_ALIGN
@@ -188,6 +191,8 @@ def test_grouped_and_training_validation(lib):
     assert wt(FAKE, FAKE, FAKE, FAKE, 16, 100, None) == L.FP8Q_ERR_SHAPE
     assert wt(FAKE, FAKE, FAKE + 8, FAKE, 16, 128, None) == L.FP8Q_ERR_ALIGN
     assert wt(FAKE, None, FAKE, FAKE, 16, 128, None) == L.FP8Q_ERR_NULL
+    assert wt(FAKE, FAKE, FAKE, FAKE, 64, 1 << 30, None) == L.FP8Q_ERR_SHAPE                    # grid x
+    assert t(FAKE, FAKE, FAKE, 1 << 31, 8, None) == L.FP8Q_ERR_SHAPE                             # grid x
     r = lib.fp8_rowwise_gemm
     assert r(FAKE, FAKE, FAKE, FAKE, FAKE, 9, 4, 4, 128, None, 0, None) == L.FP8Q_ERR_DTYPE
     assert r(FAKE, FAKE, FAKE, FAKE, FAKE, 1 | L.FP8Q_SA_KMAJOR, 4, 4, 128, None, 0, None) == L.FP8Q_ERR_DTYPE
