@@ -95,3 +95,9 @@ def test_mfma_busy_summary(tmp_path, monkeypatch):
     assert bench.measured_mfma_busy() == s["mfma_busy_frac"]
     monkeypatch.setattr(bench, "kernel_source_sha", lambda: "f" * 16)
     assert bench.measured_mfma_busy() is None
+
+
+def test_bench_rejects_unknown_workload():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--workload", "no_such_shape"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 2 and "unknown workload" in r.stderr
