@@ -82,6 +82,33 @@ def test_grouped_small_full_output(sizes, N, K, out, mode):
     assert res["violations"] == 0, res
 
 
+@pytest.mark.parametrize("E", [1024, 1000])
+def test_grouped_maximum_expert_count(E):
+    """The largest expert count the ABI takes (1024) and a count that is not a power of two:
+    the device-side scan of the per-expert tile counts (several experts per thread) and the
+    search for each tile's expert, with nearly every expert empty and rows at the first, two
+    middle and the last expert; every output against the oracle in both default modes."""
+    sizes = np.zeros(E, dtype=np.int64)
+    sizes[0], sizes[E // 2], sizes[(2 * E) // 3], sizes[E - 1] = 5, 130, 1, 3
+    N, K = 128, 256
+    offsets = offsets_of(sizes)
+    R = int(offsets[-1])
+    A = synth.random_bf16((R, K), seed=E + 1)
+    W = synth.random_bf16((E, N, K), seed=E + 2, std=0.02)
+    aq, sa, wq, sw = quantise_experts(A, W)
+    off = torch.from_numpy(offsets).cuda()
+    haq, hsa, hwq, hsw = host_codes(aq), sa.cpu().numpy(), host_codes(wq), sw.cpu().numpy()
+    y_hat, bound = oracle.grouped_gemm(haq, hsa, hwq, hsw, offsets)
+    rows, cols = np.repeat(np.arange(R), N), np.tile(np.arange(N), R)
+    for out, mode in (("bf16", "fp8"), ("f32", "exact")):
+        y = fq.fp8_grouped_gemm(aq, sa, wq, sw, off, out_dtype=TORCH_OUT[out], mode=mode)
+        torch.cuda.synchronize()
+        allow = allowances(haq, hsa, hwq, hsw, offsets, rows, cols, mode == "fp8").reshape(R, N)
+        res = gemm_check(y_host(y, out), y_hat, bound, out, allow)
+        print(f"grouped E={E} {out} {mode}", res, flush=True)
+        assert res["violations"] == 0, res
+
+
 @pytest.mark.parametrize("out,mode,config", [("bf16", "fp8", "128x256w8"), ("f32", "fp8", "128x256w8"),
                                              ("bf16", "fp8", "128x192w8"), ("f32", "exact", "128x192w8")])
 def test_grouped_bitwise_equals_per_expert_gemm(out, mode, config):
