@@ -230,6 +230,31 @@ def test_dequant_workload_full_size(name):
     assert np.array_equal(gpu_dequant(q, s), oracle.weight_dequant(q, s))
 
 
+def test_weight_quant_and_dequant_maximum_block_rows():
+    """65535 block rows, the most weight_quant's grid takes (N = 128 * 65535 - 64: a ragged
+    last block row), K = 256. Sampled block rows (the first, the last, and others) against the
+    oracle on those rows (blocks are independent), codes, scales and the dequantised weight,
+    bit for bit; the dequant runs its grid-stride loop many times at this size."""
+    N, K = 128 * 65535 - 64, 256
+    print(f"weight_quant / dequant {N}x{K}", flush=True)
+    g = torch.Generator(device="cuda").manual_seed(21)
+    w = (0.02 * torch.randn((N, K), generator=g, device="cuda", dtype=torch.float32)).to(torch.bfloat16)
+    q, sc = fq.weight_quant(w)
+    wd = fq.weight_dequant(q, sc)
+    torch.cuda.synchronize()
+    nnb = (N + 127) // 128
+    assert sc.shape == (nnb, K // 128)
+    rng = np.random.Generator(np.random.PCG64(22))
+    for nb in [0, 1, nnb // 2, nnb - 2, nnb - 1] + list(rng.integers(0, nnb, 8)):
+        r0, r1 = 128 * int(nb), min(128 * int(nb) + 128, N)
+        wb = host_bits16(w[r0:r1])
+        oq, os_ = oracle.weight_quant(wb)
+        assert np.array_equal(host_codes(q[r0:r1]), oq), nb
+        assert np.array_equal(host_f32_bits(sc[nb:nb + 1]), os_.view(np.uint32)), nb
+        assert np.array_equal(host_bits16(wd[r0:r1]), oracle.weight_dequant(oq, os_)), nb
+    del w, q, wd
+
+
 def test_quant_error_paths_on_device():
     x = torch.zeros(4, 256 + 8, dtype=torch.bfloat16, device="cuda")
     q = torch.empty(4 * 256 + 16, dtype=torch.uint8, device="cuda")
