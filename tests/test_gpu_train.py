@@ -55,6 +55,40 @@ def test_weight_transpose_bit_exact(N, K):
     assert np.array_equal(swt.cpu().numpy().view(np.uint32), os_.view(np.uint32))
 
 
+def test_act_quant_t_and_weight_transpose_large():
+    """act_quant_t over 2^22 + 3 tokens (32769 token blocks along the grid's x, a ragged
+    last block) and weight_transpose at the most 64-row tiles its grid's y takes (N = 64 *
+    65535 - 10). Sampled token blocks against the oracle on those tokens (blocks are
+    independent), and sampled column ranges of the transposed weight and its scale grid."""
+    g = torch.Generator(device="cuda").manual_seed(31)
+    M, C = (1 << 22) + 3, 64
+    print(f"act_quant_t {M}x{C}", flush=True)
+    x = torch.randn((M, C), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    qt, st = fq.act_quant_t(x)
+    torch.cuda.synchronize()
+    nmb = (M + 127) // 128
+    assert qt.shape == (C, nmb * 128) and st.shape == (C, nmb)
+    rng = np.random.Generator(np.random.PCG64(32))
+    for mb in [0, 1, nmb // 2, nmb - 1] + list(rng.integers(0, nmb, 6)):
+        t0, t1 = 128 * int(mb), min(128 * int(mb) + 128, M)
+        oq, os_ = oracle.act_quant_t(host_bits16(x[t0:t1]))
+        assert np.array_equal(host_codes(qt[:, 128 * mb:128 * mb + 128].contiguous()), oq), mb
+        assert np.array_equal(st[:, mb:mb + 1].contiguous().cpu().numpy().view(np.uint32), os_.view(np.uint32)), mb
+    del x, qt, st
+    N, K = 64 * 65535 - 10, 256
+    print(f"weight_transpose {N}x{K}", flush=True)
+    w = (0.02 * torch.randn((N, K), generator=g, device="cuda", dtype=torch.float32)).to(torch.bfloat16)
+    wq, sw = fq.weight_quant(w)
+    del w
+    wqt, swt = fq.weight_transpose(wq, sw)
+    torch.cuda.synchronize()
+    assert wqt.shape == (K, N) and swt.shape == (K // 128, (N + 127) // 128)
+    for n0 in [0, 64, N // 2 - N // 2 % 64, N - 300] + [int(v) * 64 for v in rng.integers(0, N // 64, 4)]:
+        n1 = min(n0 + 300, N)
+        assert np.array_equal(host_codes(wqt[:, n0:n1].contiguous()), host_codes(wq[n0:n1]).T), n0
+    assert torch.equal(swt.view(torch.int32), sw.t().contiguous().view(torch.int32))
+
+
 class RowwiseReference:
     """The oracle's full per-row GEMM and the per-output allowances of one operand set
     (computed once, reused across modes and configurations)."""
