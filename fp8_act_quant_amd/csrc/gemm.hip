@@ -864,18 +864,24 @@ __global__ __launch_bounds__(NW * 64) void block_gemm_kernel(GemmArgs g) {
         __syncthreads();
         if (!*flag) return;
         // the last to arrive sums the partials in split order (independent of which split
-        // arrived last), one row group at a time; its own partial is read back like the
-        // others (the loads of a row group are all issued before the first is needed)
+        // arrived last), one row group at a time; its own partial is taken from its registers
+        // (the values it stored), the others' are loaded (the loads of a row group are all
+        // issued before the first is needed)
 #pragma unroll
         for (int i = 0; i < SUB_M; ++i) {
             f32x4 t[SUB_N];
             for (int sp = 0; sp < g.splits; ++sp) {
                 f32x4 v[SUB_N];
+                if (sp == split) {
 #pragma unroll
-                for (int j = 0; j < SUB_N; ++j)
-                    v[j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                         rp, lane_off + (i * SUB_N + j) * 1024, sp * (BM * BN * 4),
-                                                         kDeviceScope));
+                    for (int j = 0; j < SUB_N; ++j) v[j] = acc[i][j];
+                } else {
+#pragma unroll
+                    for (int j = 0; j < SUB_N; ++j)
+                        v[j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                             rp, lane_off + (i * SUB_N + j) * 1024,
+                                                             sp * (BM * BN * 4), kDeviceScope));
+                }
 #pragma unroll
                 for (int j = 0; j < SUB_N; ++j) t[j] = sp == 0 ? v[j] : t[j] + v[j];
             }
