@@ -1,22 +1,25 @@
 #!/usr/bin/env python3
 """Throughput of the FP8 block-scaled path on one MI355X.
 
-One step = fp8_act_quant_kmajor(A) -> fp8_block_gemm(Aq, sa, Wq, sw) -> Y on the query
-down-projection workload (A 4096x7168 bf16 tokens, W 1536x7168 pre-quantised to E4M3
-128x128 blocks, Y bf16). The activation scales are written and read K-block-major
-([K/128, M], the layout in which the GEMM fetches one K slice's scales as whole lines). Weights are quantised once before timing (offline, as stored
+One step = fp8_act_quant_kmajor(A) -> fp8_block_gemm(Aq, sa, Wq, sw) -> Y. The default
+workload is the largest one, the outlier-stress square GEMM (A 16384x7168 bf16 tokens with
+0.1% of channels x100, W 7168x7168 with 1% of 128x128 blocks x50, pre-quantised to E4M3,
+Y fp32 in the library's default contraction for fp32 output: exact f16 slices).
+`--workload` selects another (q_down, kv_down, kv_up, tiny). The activation scales are
+written and read K-block-major ([K/128, M], the layout in which the GEMM fetches one K
+slice's scales as whole lines). Weights are quantised once before timing (offline, as stored
 FP8 weights are). Inputs are resident in HBM; A is rotated over several copies so that
-act_quant reads HBM rather than the 256 MB last-level cache. The default warm-up (2000
-untimed steps, ~0.15 s) is sized to the part's clock ramp: under sustained load the
-step time falls for the first ~500-1000 steps and then holds, so the timed steps measure
-the steady state.
+act_quant reads HBM rather than the 256 MB last-level cache. The warm-up is sized to the
+part's clock ramp: under sustained load the step time falls for the first ~0.1-0.2 s and
+then holds, so the timed steps measure the steady state.
 
 Prints ONE JSON line. `value` = 2*M*N*K / (time per step) in TFLOP/s, i.e. GEMM flops
-per second including the activation quantisation. `roofline` is for the dominant
-kernel (the GEMM) with its duration measured by HIP events around each launch on the
-stream it runs on (events without the system-scope fence, see TimingEvent); act_quant's
-HBM figures are reported beside it. `cpu_baseline`
-times the CPU oracle (as it is) on a bounded row sample of the same workload.
+per second including the activation quantisation, from the back-to-back timed steps.
+`roofline` is for the dominant kernel (the GEMM) with its duration measured by HIP events
+around each launch on the stream it runs on (events without the system-scope fence, see
+TimingEvent); median, p10 and p90 of those per-launch durations are given beside the mean.
+act_quant's HBM figures are reported beside it. `cpu_baseline` times the CPU oracle (as it
+is) on a bounded row sample of the same workload.
 """
 from __future__ import annotations
 
@@ -34,8 +37,14 @@ FP8_PEAK_TFLOPS = 5000.0      # MI355X dense FP8 MFMA
 F16_PEAK_TFLOPS = 2500.0      # MI355X dense f16 MFMA (the exact-slice contraction)
 HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
 METRIC = "fp8_block_gemm TFLOP/s (incl. act_quant) and % of MI355X FP8 MFMA peak"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_q_down_traffic.json")
-MFMA_FILE = os.path.join(ROOT, "profiles", "gemm_q_down_mfma_busy.json")
+
+
+def traffic_file(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"gemm_{workload}_traffic.json")
+
+
+def mfma_file(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"gemm_{workload}_mfma_busy.json")
 # MI355X: GRBM_GUI_ACTIVE is reported once per XCD (8) and summed; SQ_VALU_MFMA_BUSY_CYCLES is
 # summed over every SIMD (256 CUs x 4), so busy / (GUI_ACTIVE / XCDS * SIMDS) is the fraction of
 # the kernel's cycles in which the average SIMD's matrix unit was busy (rocprofv3's MfmaUtil)
@@ -115,20 +124,27 @@ def _stored(path: str, key: str):
     return t.get(key)
 
 
-def measured_mfma_busy():
-    """The GEMM's matrix-unit busy fraction from the committed counter summary, or None."""
-    return _stored(MFMA_FILE, "mfma_busy_frac")
+def measured_mfma_busy(workload: str):
+    """The GEMM's matrix-unit busy fraction on a workload from the committed counter
+    summary, or None."""
+    return _stored(mfma_file(workload), "mfma_busy_frac")
 
 
-def write_mfma_summary(csv_path: str) -> dict:
-    """Matrix-unit busy fraction of the q_down GEMM from one rocprofv3 --pmc run with
+def _workload_label(workload: str) -> str:
+    import synth
+    wl = synth.WORKLOADS[workload]
+    return f"{wl.name} {wl.M}x{wl.N}x{wl.K} {wl.out_dtype} out"
+
+
+def write_mfma_summary(csv_path: str, workload: str) -> dict:
+    """Matrix-unit busy fraction of a workload's GEMM from one rocprofv3 --pmc run with
     SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE, stored with the kernel source hash."""
     busy = _per_dispatch(csv_path, "SQ_VALU_MFMA_BUSY_CYCLES")["gemm"]
     active = _per_dispatch(csv_path, "GRBM_GUI_ACTIVE")["gemm"]
     cycles = active / XCDS
     summary = {
         "kernel_source_sha": kernel_source_sha(),
-        "workload": "q_down 4096x1536x7168 bf16 out",
+        "workload": _workload_label(workload),
         "sq_valu_mfma_busy_cycles_per_dispatch": round(busy, 1),
         "grbm_gui_active_per_dispatch": round(active, 1),
         "xcds": XCDS,
@@ -136,15 +152,15 @@ def write_mfma_summary(csv_path: str) -> dict:
         "kernel_cycles": round(cycles, 1),
         "mfma_busy_frac": round(busy / (cycles * SIMDS), 4),
     }
-    with open(MFMA_FILE, "w") as f:
+    with open(mfma_file(workload), "w") as f:
         json.dump(summary, f, indent=1)
     return summary
 
 
-def measured_traffic():
-    """HBM bytes per GEMM launch from the committed counter summary, if it was taken on
-    the current kernel source; otherwise None."""
-    return _stored(TRAFFIC_FILE, "hbm_bytes_per_launch")
+def measured_traffic(workload: str):
+    """HBM bytes per GEMM launch on a workload from the committed counter summary, if it
+    was taken on the current kernel source; otherwise None."""
+    return _stored(traffic_file(workload), "hbm_bytes_per_launch")
 
 
 COPY_BYTES = 256 << 20   # bytes read (and written) by the calibration copy
@@ -174,7 +190,7 @@ def _per_dispatch(csv_path: str, counter: str):
     return {k: sum(v) / len(v) for k, v in out.items()}
 
 
-def write_traffic_summary(fetch_csv: str, write_csv: str) -> dict:
+def write_traffic_summary(fetch_csv: str, write_csv: str, workload: str) -> dict:
     """HBM bytes per GEMM (and act_quant) launch from FETCH_SIZE and WRITE_SIZE (KiB per
     dispatch), each scaled by what the same counter reads for the calibration copy of
     COPY_BYTES; stored with the hash of the kernel source it was taken on."""
@@ -183,7 +199,7 @@ def write_traffic_summary(fetch_csv: str, write_csv: str) -> dict:
     w_scale = COPY_BYTES / (write["copy"] * 1024.0)
     summary = {
         "kernel_source_sha": kernel_source_sha(),
-        "workload": "q_down 4096x1536x7168 bf16 out",
+        "workload": _workload_label(workload),
         "fetch_kib_per_dispatch": {k: round(v, 1) for k, v in fetch.items()},
         "write_kib_per_dispatch": {k: round(v, 1) for k, v in write.items()},
         "copy_scale": {"fetch": round(f_scale, 4), "write": round(w_scale, 4), "copy_bytes": COPY_BYTES},
@@ -191,9 +207,37 @@ def write_traffic_summary(fetch_csv: str, write_csv: str) -> dict:
         "act_quant_hbm_bytes_per_launch": round(fetch["act_quant"] * 1024.0 * f_scale +
                                                 write["act_quant"] * 1024.0 * w_scale),
     }
-    with open(TRAFFIC_FILE, "w") as f:
+    with open(traffic_file(workload), "w") as f:
         json.dump(summary, f, indent=1)
     return summary
+
+
+def host_cpu() -> dict:
+    """The host CPU the oracle ran on: logical CPUs the process may use, the machine's
+    count, and the model name from /proc/cpuinfo."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count()
+    return {"nproc": usable, "cpu_count": os.cpu_count(), "cpu_model": model}
+
+
+# multiply-adds of the CPU-baseline GEMM sample: about 2.5 s on 16 threads of the oracle
+CPU_SAMPLE_MACS = 1.0e11
+
+
+def cpu_sample_rows(M: int, N: int, K: int) -> int:
+    rows = int(CPU_SAMPLE_MACS // (N * K))
+    return max(1, min(M, rows - rows % 64 if rows >= 64 else rows))
 
 
 def cpu_baseline(A, W, rows: int):
@@ -219,7 +263,13 @@ def cpu_baseline(A, W, rows: int):
         "kind": "oracle",
         "sample": f"first {rows} of {M} tokens: act_quant {rows}x{K} + float64 block GEMM {rows}x{N}x{K} "
                   f"(act_quant {t1 - t0:.2f}s, gemm {t2 - t1:.2f}s wall)",
+        "host": {**host_cpu(), "omp_threads": oracle.num_threads()},
     }, (aq, sa, y)
+
+
+def _pct(t, q) -> float:
+    import numpy as np
+    return round(float(np.percentile(t, q)) * 1e6, 3)
 
 
 def grouped_measurement(fq, L, synth, dev, stream, steps: int, warmup: int) -> dict:
@@ -341,31 +391,41 @@ def backward_measurement(fq, dev, stream, steps: int, warmup: int) -> dict:
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=500)
-    ap.add_argument("--warmup", type=int, default=2000)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default: about 0.7 s of steps, at least 50)")
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps before timing (default: about 0.3 s of steps, at least 20)")
     ap.add_argument("--copies", type=int, default=10, help="rotated copies of A")
-    ap.add_argument("--workload", default="q_down",
-                    help="synthetic workload (q_down, the headline; kv_down, kv_up, outlier, tiny for their own "
-                         "figures, in their default contraction mode: FP8 products for bf16 output, exact slices "
-                         "for fp32)")
-    ap.add_argument("--cpu-rows", type=int, default=4096, help="token rows in the CPU-baseline sample")
+    ap.add_argument("--settle-s", type=float, default=0.3,
+                    help="minimum seconds of untimed steps before timing (clock ramp); 0 for counter runs")
+    ap.add_argument("--workload", default=None,
+                    help="synthetic workload (outlier, the headline and default; q_down, kv_down, kv_up, tiny for "
+                         "their own figures), in its default contraction mode: FP8 products for bf16 output, exact "
+                         "slices for fp32")
+    ap.add_argument("--cpu-rows", type=int, default=0,
+                    help="token rows in the CPU-baseline sample (default: about 1e11 multiply-adds)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the routed-expert GEMM measurement")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the timed steps, run a plain device copy of known size (for counter scaling); "
                          "skips the routed-expert measurement")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="write the GEMM's HBM traffic summary from two rocprofv3 --pmc runs and exit")
+                    help="write the workload's GEMM HBM traffic summary from two rocprofv3 --pmc runs and exit")
     ap.add_argument("--mfma-from", metavar="PMC_CSV",
-                    help="write the GEMM's matrix-unit busy summary from a rocprofv3 --pmc run of "
+                    help="write the workload's GEMM matrix-unit busy summary from a rocprofv3 --pmc run of "
                          "SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE and exit")
     args = ap.parse_args()
 
+    import synth
+    workload = args.workload or synth.HEADLINE
+    if workload not in synth.WORKLOADS:
+        print(f"unknown workload {workload}; one of {sorted(synth.WORKLOADS)}", file=sys.stderr)
+        return 2
     if args.traffic_from:
-        print(json.dumps(write_traffic_summary(*args.traffic_from)), flush=True)
+        print(json.dumps(write_traffic_summary(*args.traffic_from, workload)), flush=True)
         return 0
     if args.mfma_from:
-        print(json.dumps(write_mfma_summary(args.mfma_from)), flush=True)
+        print(json.dumps(write_mfma_summary(args.mfma_from, workload)), flush=True)
         return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -377,14 +437,9 @@ def main() -> int:
     import torch
 
     import fp8_act_quant_amd as fq
-    import synth
     from fp8_act_quant_amd import _lib as L
 
-    if args.workload not in synth.WORKLOADS:
-        print(f"unknown workload {args.workload}; one of {sorted(synth.WORKLOADS)}", file=sys.stderr)
-        return 2
-    wl = synth.WORKLOADS[args.workload]
-    headline = wl.name == synth.HEADLINE
+    wl = synth.WORKLOADS[workload]
     M, N, K = wl.M, wl.N, wl.K
     out_bf16 = wl.out_dtype == "bf16"
     exact = not out_bf16   # the library's default contraction for fp32 output
@@ -404,7 +459,7 @@ def main() -> int:
     sptr = stream.cuda_stream
     out_code = (L.FP8Q_OUT_BF16 if out_bf16 else L.FP8Q_OUT_F32) | L.FP8Q_SA_KMAJOR
     ws_bytes = fq.gemm_workspace_bytes(M, N, K, y.dtype)
-    ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device=dev)   # zero-filled before first use
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)   # split-K workspace (any contents)
     lib = fq.lib
     p_aq, p_sa, p_wq, p_sw, p_y, p_ws = aq.data_ptr(), sa.data_ptr(), wq.data_ptr(), sw.data_ptr(), \
         y.data_ptr(), ws.data_ptr()
@@ -421,32 +476,51 @@ def main() -> int:
         if ev is not None:
             ev[2].record(stream)
 
-    for i in range(args.warmup):
+    # step counts: a calibration step gives the step time, then the defaults are about 0.3 s of
+    # warm-up (past the clock ramp) and 0.7 s of timed steps
+    t_cal = time.perf_counter()
+    for i in range(5):
         step(i)
     torch.cuda.synchronize()
+    est = max((time.perf_counter() - t_cal) / 5, 1e-6)
+    warmup = args.warmup if args.warmup is not None else max(20, int(0.3 / est))
+    steps = args.steps if args.steps is not None else max(50, int(0.7 / est))
+    t_w = time.perf_counter()
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # Clock settle: the part's clock ramps up over its first ~0.1-0.3 s under load. When the
+    # requested warm-up is shorter than that, more untimed steps follow (reported as
+    # clock_settle_steps) so that the timed steps see the steady clock.
+    settle = 0
+    while time.perf_counter() - t_w < args.settle_s:
+        for _ in range(max(1, int(0.05 / est))):
+            step(warmup + settle)
+            settle += 1
+        torch.cuda.synchronize()
 
     # timed region 1: back-to-back steps, whole-step throughput
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record(stream)
-    for i in range(args.steps):
+    for i in range(steps):
         step(i)
     t_end.record(stream)
     torch.cuda.synchronize()
     ms_total = t_start.elapsed_time(t_end)
-    ms_per_step = ms_total / args.steps
+    ms_per_step = ms_total / steps
 
     # timed region 2: the same steps with an event around each launch (per-kernel durations)
-    evs = [[TimingEvent() for _ in range(3)] for _ in range(args.steps)]
+    evs = [[TimingEvent() for _ in range(3)] for _ in range(steps)]
     torch.cuda.synchronize()
-    for i in range(args.steps):
+    for i in range(steps):
         step(i, evs[i])
     torch.cuda.synchronize()
     t_aq = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e-3
 
     # act_quant alone, launches back to back over the rotated copies (events only around the
     # loop): its per-launch time without the dispatch latency a per-launch event pair exposes
-    b2b_n = max(args.steps, 100)
+    b2b_n = max(steps, 100)
     a0_ev, a1_ev = TimingEvent(), TimingEvent()
     torch.cuda.synchronize()
     a0_ev.record(stream)
@@ -462,8 +536,7 @@ def main() -> int:
     gemm_tflops = flops / t_gemm.mean() / 1e12
     aq_bytes = M * K * 2 + M * K + M * (K // 128) * 4
     aq_gbs = aq_bytes / t_aq.mean() / 1e9
-    # the stored counter summaries are the headline workload's
-    traffic = measured_traffic() if headline else None
+    traffic = measured_traffic(wl.name)
     # exact slices contract on the f16 matrix unit (dense 2.5 PF)
     peak = F16_PEAK_TFLOPS if exact else FP8_PEAK_TFLOPS
 
@@ -472,8 +545,9 @@ def main() -> int:
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
+        "clock_settle_steps": settle,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -493,9 +567,12 @@ def main() -> int:
             "frac": round(gemm_tflops / peak, 4),
             "traffic": traffic,
             # rocprof MFMA-busy counters (matrix unit busy over the kernel's cycles at its own clock)
-            "mfma_busy_frac": measured_mfma_busy() if headline else None,
+            "mfma_busy_frac": measured_mfma_busy(wl.name),
             "avg_launch_us": round(float(t_gemm.mean()) * 1e6, 3),
+            "launch_us_median_p10_p90": [_pct(t_gemm, 50), _pct(t_gemm, 10), _pct(t_gemm, 90)],
             "algorithmic_flops_per_launch": flops,
+            "contraction": "exact f16 slices (f16 matrix unit)" if exact else "FP8 products (FP8 matrix unit)",
+            "counter_files": [os.path.relpath(traffic_file(wl.name), ROOT), os.path.relpath(mfma_file(wl.name), ROOT)],
         },
         "act_quant": {
             "kernel": "act_quant_kernel",
@@ -505,6 +582,7 @@ def main() -> int:
             "unit": "GB/s",
             "frac": round(aq_gbs / HBM_PEAK_GBS, 4),
             "avg_launch_us": round(float(t_aq.mean()) * 1e6, 3),
+            "launch_us_median_p10_p90": [_pct(t_aq, 50), _pct(t_aq, 10), _pct(t_aq, 90)],
             "algorithmic_bytes_per_launch": aq_bytes,
             "back_to_back_us": round(t_aq_b2b * 1e6, 3),
             "back_to_back_frac": round(aq_bytes / t_aq_b2b / 1e9 / HBM_PEAK_GBS, 4),
@@ -514,12 +592,11 @@ def main() -> int:
 
     if not args.no_extras and not args.calibrate_copy:   # (counter runs: the calibration kernel must be the only multiply)
         # (the part is at its steady clock by now; a shorter warm-up suffices for these)
-        result["grouped_gemm"] = grouped_measurement(fq, L, synth, dev, stream, args.steps, min(args.warmup, 300))
-        result["training_backward"] = backward_measurement(fq, dev, stream, min(args.steps, 50),
-                                                           min(args.warmup, 300))
+        result["grouped_gemm"] = grouped_measurement(fq, L, synth, dev, stream, 200, 300)
+        result["training_backward"] = backward_measurement(fq, dev, stream, 50, 300)
 
     if not args.no_cpu_baseline:
-        r = min(args.cpu_rows, M)
+        r = min(args.cpu_rows, M) if args.cpu_rows > 0 else cpu_sample_rows(M, N, K)
         cb, (oaq, osa, oy) = cpu_baseline(A_host, W_host, r)
         # sanity: the GPU path on the same rows agrees with the oracle (codes exactly)
         gpu_codes = aq[:r].view(torch.uint8).cpu().numpy()

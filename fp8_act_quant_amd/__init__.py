@@ -128,9 +128,8 @@ def gemm_workspace_bytes(M: int, N: int, K: int, out_dtype=torch.bfloat16, mode:
     return int(lib.fp8_block_gemm_workspace_bytes(M, N, K, _gemm_code(out_dtype, mode)))
 
 
-# Split-K workspaces kept per (device, stream): zero-filled once, and left ready for reuse
-# by every call (the library resets its arrival counters). One per stream, because calls
-# that may overlap must not share one.
+# Split-K workspaces kept per (device, stream) and reused by every call (the library needs
+# no initialised contents). One per stream, because calls that may overlap must not share one.
 _WORKSPACES: dict = {}
 
 
@@ -138,7 +137,7 @@ def _auto_workspace(device: torch.device, stream: int, nbytes: int) -> torch.Ten
     key = (device.index, stream)
     ws = _WORKSPACES.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        ws = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
         _WORKSPACES[key] = ws
     return ws
 
@@ -173,8 +172,8 @@ def fp8_gemm(a: torch.Tensor, a_s: torch.Tensor, w: torch.Tensor, w_s: torch.Ten
     f16 matrix unit from exactly converted operands; "default" is "exact" for float32
     output and "fp8" for bfloat16 output.
 
-    workspace: "auto" (a zero-initialised workspace cached per device and stream), None
-    (no split-K), or a uint8 tensor that was zero-filled before its first use.
+    workspace: "auto" (a workspace cached per device and stream), None (no split-K), or a
+    uint8 tensor of any contents.
 
     bias: optional [N] vector, added in fp32 to every row before the output rounding."""
     if mode not in _MODES:

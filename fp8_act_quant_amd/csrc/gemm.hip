@@ -45,9 +45,11 @@
 //
 // Split-K. For shapes with too few tiles to fill the 256 CUs the K slices are divided into
 // `splits` contiguous ranges. Each workgroup stores its fp32 partial tile to the caller's
-// workspace and bumps the tile's arrival counter; the last to arrive adds the partials in
-// split order (so the result does not depend on arrival order), writes Y and resets the
-// counter to zero.
+// workspace and counts its arrival in the tile's arrival word; the last to arrive adds the
+// partials in split order (so the result does not depend on arrival order) and writes Y.
+// Arrival words carry the launch's epoch (a host counter) beside the count: a word holding
+// another epoch counts as zero arrivals, so a workspace needs no clearing before its first
+// use and a call that never completed leaves nothing that a later call would misread.
 #include <atomic>
 #include <cstdlib>
 #include <cstring>
@@ -345,7 +347,8 @@ struct GemmArgs {
     void *y;
     const float *bias;  // [N] fp32 added to every row before the output rounding, or null
     float *part;        // split-K partial tiles [splits][tiles][BM * BN], or null
-    uint32_t *count;    // split-K arrival counter per tile, zero between calls
+    uint64_t *count;    // split-K arrival word per tile: (epoch << 32) | arrivals
+    uint32_t epoch;     // this launch's epoch (non-zero)
     // grouped (per-expert) GEMM: expert e owns rows [offsets[e], offsets[e+1]) of A and Y and
     // the weight wq + e*N*K (scales sw + e*ceil(N/128)*K/128); null for a plain GEMM
     const int64_t *offsets;
@@ -837,12 +840,19 @@ __global__ __launch_bounds__(NW * 64) void block_gemm_kernel(GemmArgs g) {
 
     if (g.splits > 1) {
         // split-K: publish this split's partial tile (fragment order: one 1 KiB line per
-        // (wave, i, j), lane-contiguous) with device-coherent stores (sc1: written through
-        // to memory, visible to every XCD once the store has completed), then count
-        // arrivals. No release/acquire fence is used: at device scope those write back or
-        // invalidate the whole L2, which costs more than the partials themselves; the
-        // partial traffic itself is coherent and the counter is bumped only after the
-        // stores have completed (vmcnt 0).
+        // (wave, i, j), lane-contiguous), then count the arrival. Ordering argument, after
+        // the LLVM AMDGPU backend user guide's memory model for gfx942 (whose code sequences
+        // gfx950 shares): a relaxed agent-scope atomic load, store or read-modify-write is
+        // the plain instruction with the sc1 (agent scope) bit; release and acquire at agent
+        // scope add only an L2 write-back before (buffer_wbl2 sc1) and an invalidate after
+        // (buffer_inv sc1), which serve other, non-atomic data. Here every access to the
+        // exchanged data is such an agent-scope access: the partials are stored and reloaded
+        // with sc1 buffer instructions, the arrival word is an agent-scope atomic. The stores
+        // have completed (vmcnt 0) before the arrival is counted, and the last workgroup
+        // issues its loads only after its atomic has returned and its workgroup barrier, so
+        // it reads every partial. The cache maintenance is left out on purpose: at agent
+        // scope it writes back or invalidates the whole L2, which costs more than the
+        // partials themselves.
         const rsrc_t rp = make_rsrc(g.part + (int64_t)tl * g.splits * (BM * BN), (int64_t)g.splits * BM * BN * 4);
         const uint32_t lane_off = (uint32_t)((wave * (SUB_M * SUB_N * 64) + lane) * 16);
         const int split_off = split * (BM * BN * 4);
@@ -856,9 +866,23 @@ __global__ __launch_bounds__(NW * 64) void block_gemm_kernel(GemmArgs g) {
         __syncthreads();
         int *flag = reinterpret_cast<int *>(smem + S::FLAG);
         if (threadIdx.x == 0) {
-            const uint32_t old = __hip_atomic_fetch_add(&g.count[tl], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            const int last = old == (uint32_t)(g.splits - 1);
-            if (last) __hip_atomic_store(&g.count[tl], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            // count this arrival: a word of another epoch (stale, or never written) is zero
+            // arrivals of this one. The last arrival sets the count back to zero, so a launch
+            // replayed with the same epoch (a captured graph) starts from zero as well.
+            uint64_t *word = &g.count[tl];
+            uint64_t cur = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            uint32_t arrived;
+            for (;;) {
+                const uint32_t c = (uint32_t)(cur >> 32) == g.epoch ? (uint32_t)cur : 0u;
+                const uint64_t next = ((uint64_t)g.epoch << 32) | (uint64_t)(c + 1);
+                if (__hip_atomic_compare_exchange_strong(word, &cur, next, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                         __HIP_MEMORY_SCOPE_AGENT)) {
+                    arrived = c + 1;
+                    break;
+                }
+            }
+            const int last = arrived == (uint32_t)g.splits;
+            if (last) __hip_atomic_store(word, (uint64_t)g.epoch << 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             *flag = last;
         }
         __syncthreads();
@@ -1068,10 +1092,22 @@ bool gemm_force_config(int tile, int splits) {
 
 const char *gemm_config_name(int tile) { return tile >= 0 && tile < T_COUNT ? kTiles[tile].name : nullptr; }
 
-// Split-K workspace: the arrival counters first, at a fixed place whatever the shape (a
-// later call with another shape must find zeros there), then the partial tiles.
+// Split-K workspace: the arrival words first, at a fixed place whatever the shape, then the
+// partial tiles.
 constexpr int64_t kMaxSplitTiles = 4096;
-constexpr size_t kCounterBytes = kMaxSplitTiles * sizeof(uint32_t);
+constexpr size_t kCounterBytes = kMaxSplitTiles * sizeof(uint64_t);
+
+// Epoch of a split-K launch: never 0, so that a zero-filled workspace holds no arrivals of
+// any launch. Launches that share a workspace run one after the other on one stream, so
+// they only need different epochs, which a process-wide counter gives (until it wraps
+// after 2^32 - 1 launches).
+static std::atomic<uint32_t> g_epoch{0};
+static uint32_t next_epoch() {
+    uint32_t e;
+    do e = g_epoch.fetch_add(1, std::memory_order_relaxed) + 1;
+    while (e == 0);
+    return e;
+}
 
 static size_t split_bytes(const GemmPlan &p) {
     if (p.splits <= 1) return 0;
@@ -1125,6 +1161,7 @@ static GemmPlan make_plan(int64_t M, int64_t N, int64_t K, bool exact, size_t ws
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, bool, bool exact, bool rowb) {
     return split_bytes(make_plan(M, N, K, exact, 0, true, rowb));
 }
+
 
 template <int BM, int BN, int NW, int WAVES_M, int NSTAGE, int EXACT, int GROUPED = 0, int ROWB = 0>
 static hipError_t launch_cfg(GemmArgs a, bool out_bf16, int splits, hipStream_t stream) {
@@ -1186,9 +1223,10 @@ hipError_t launch_rowwise_gemm(const uint8_t *aq, const float *sa, const uint8_t
                                size_t workspace_bytes, hipStream_t stream) {
     if (M == 0 || N == 0) return hipSuccess;
     const GemmPlan p = make_plan(M, N, K, exact, workspace ? workspace_bytes : 0, false, true);
-    GemmArgs a{aq, sa, bq, sb, y, nullptr, nullptr, nullptr, nullptr, M, N, K, 0, 0, 1, 1, 0, 0};
+    GemmArgs a{aq, sa, bq, sb, y, nullptr, nullptr, nullptr, 0, nullptr, M, N, K, 0, 0, 1, 1, 0, 0};
     if (p.splits > 1) {
-        a.count = static_cast<uint32_t *>(workspace);
+        a.count = static_cast<uint64_t *>(workspace);
+        a.epoch = next_epoch();
         a.part = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + kCounterBytes);
     }
     return dispatch_rowb(p, a, out_bf16, exact, stream);
@@ -1200,9 +1238,10 @@ hipError_t launch_block_gemm(const uint8_t *aq, const float *sa, const uint8_t *
     if (M == 0 || N == 0) return hipSuccess;
     if (sa_kmajor && M * (K / G_SLICE) >= ((int64_t)1 << 29)) return hipErrorInvalidValue;
     const GemmPlan p = make_plan(M, N, K, exact, workspace ? workspace_bytes : 0, false);
-    GemmArgs a{aq, sa, wq, sw, y, bias, nullptr, nullptr, nullptr, M, N, K, 0, 0, 1, 1, 0, sa_kmajor ? 1 : 0};
+    GemmArgs a{aq, sa, wq, sw, y, bias, nullptr, nullptr, 0, nullptr, M, N, K, 0, 0, 1, 1, 0, sa_kmajor ? 1 : 0};
     if (p.splits > 1) {
-        a.count = static_cast<uint32_t *>(workspace);
+        a.count = static_cast<uint64_t *>(workspace);
+        a.epoch = next_epoch();
         a.part = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + kCounterBytes);
     }
     return dispatch(p, a, out_bf16, exact, stream);
@@ -1214,7 +1253,7 @@ hipError_t launch_grouped_gemm(const uint8_t *aq, const float *sa, const uint8_t
     if (rows == 0 || N == 0) return hipSuccess;
     // Few tiles are instantiated for the grouped kernel: BM = 128 keeps the padding of each
     // expert's last m-tile small; BN = 256 for wide weights, 192 otherwise.
-    GemmArgs a{aq, sa, wq, sw, y, nullptr, nullptr, nullptr, offsets, rows, N, K, 0, 0, 1, 1, (int)experts, 0};
+    GemmArgs a{aq, sa, wq, sw, y, nullptr, nullptr, nullptr, 0, offsets, rows, N, K, 0, 0, 1, 1, (int)experts, 0};
     if (exact) return launch_cfg<128, 192, 8, 2, 3, 1, 1>(a, out_bf16, 1, stream);
     if (N >= 1024) return launch_cfg<128, 256, 8, 2, 3, 0, 1>(a, out_bf16, 1, stream);
     return launch_cfg<128, 192, 8, 2, 3, 0, 1>(a, out_bf16, 1, stream);

@@ -139,10 +139,10 @@ int fp8_weight_dequant(const uint8_t *q, const float *s, uint16_t *w, int64_t N,
  *   workspace / workspace_bytes: optional device scratch (16-byte aligned) for a split-K
  *   schedule, used by shapes with too few output tiles to fill the GPU; pass NULL / 0 to run
  *   without it. If workspace_bytes is smaller than fp8_block_gemm_workspace_bytes() the call
- *   runs without split-K (it does not fail). The workspace must be zero-filled before its
- *   first use; every call that completes leaves it ready for the next (its arrival counters
- *   back at zero), so zero it once and reuse it. Calls that may run at the same time must
- *   not share a workspace.
+ *   runs without split-K (it does not fail). The workspace needs no initialisation: its
+ *   arrival words are tagged with a per-launch epoch, so any contents, including those left
+ *   by a call that never completed, count as no arrivals. Calls that may run at the same
+ *   time must not share a workspace.
  *   The result does not depend on whether a workspace is given beyond fp32 rounding
  *   order (split-K sums the K ranges' fp32 partials in a fixed order), and is deterministic
  *   for a given (M, N, K, workspace size) call. */

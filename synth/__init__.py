@@ -59,8 +59,8 @@ WORKLOADS = {
     ]
 }
 
-# the workload the headline throughput figure is quoted on
-HEADLINE = "q_down"
+# the workload the headline throughput figure is quoted on: the largest (1.68 TFLOP per step)
+HEADLINE = "outlier"
 
 
 @dataclass(frozen=True)

@@ -49,8 +49,9 @@ def test_traffic_summary_scaling_and_hash(tmp_path, monkeypatch):
     _write_csv(f, "FETCH_SIZE", [(1, COPY, kib / 2), (2, GEMM, 1000.0), (3, AQ, 300.0)])
     _write_csv(w, "WRITE_SIZE", [(1, COPY, kib), (2, GEMM, 200.0), (3, AQ, 100.0)])
     out = tmp_path / "traffic.json"
-    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(out))
-    s = bench.write_traffic_summary(str(f), str(w))
+    monkeypatch.setattr(bench, "traffic_file", lambda wl: str(out))
+    s = bench.write_traffic_summary(str(f), str(w), "kv_down")
+    assert s["workload"].startswith("kv_down 4096x576x7168")
     assert s["copy_scale"]["fetch"] == pytest.approx(2.0) and s["copy_scale"]["write"] == pytest.approx(1.0)
     assert s["hbm_bytes_per_launch"] == round(1000.0 * 1024 * 2 + 200.0 * 1024)
     assert s["act_quant_hbm_bytes_per_launch"] == round(300.0 * 1024 * 2 + 100.0 * 1024)
@@ -58,7 +59,7 @@ def test_traffic_summary_scaling_and_hash(tmp_path, monkeypatch):
     assert json.load(open(out)) == s
     # the bench reports the stored figure only while the kernel source is unchanged
     monkeypatch.setattr(bench, "kernel_source_sha", lambda: "0" * 16)
-    assert bench.measured_traffic() is None
+    assert bench.measured_traffic("kv_down") is None
 
 
 def test_more_than_one_gpu_is_refused():
@@ -87,17 +88,40 @@ def test_mfma_busy_summary(tmp_path, monkeypatch):
         w.writerow({"Dispatch_Id": 3, "Kernel_Name": AQ, "Counter_Name": "SQ_VALU_MFMA_BUSY_CYCLES",
                     "Counter_Value": 1e12})
     out = tmp_path / "mfma.json"
-    monkeypatch.setattr(bench, "MFMA_FILE", str(out))
-    s = bench.write_mfma_summary(str(p))
+    monkeypatch.setattr(bench, "mfma_file", lambda wl: str(out))
+    s = bench.write_mfma_summary(str(p), "outlier")
+    assert s["workload"].startswith("outlier 16384x7168x7168")
     # mean busy 384000 over 1000 cycles x 1024 SIMDs
     assert s["kernel_cycles"] == pytest.approx(1000.0)
     assert s["mfma_busy_frac"] == pytest.approx(384000.0 / (1000.0 * 1024), abs=1e-4)
-    assert bench.measured_mfma_busy() == s["mfma_busy_frac"]
+    assert bench.measured_mfma_busy("outlier") == s["mfma_busy_frac"]
     monkeypatch.setattr(bench, "kernel_source_sha", lambda: "f" * 16)
-    assert bench.measured_mfma_busy() is None
+    assert bench.measured_mfma_busy("outlier") is None
 
 
 def test_bench_rejects_unknown_workload():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--workload", "no_such_shape"],
                        capture_output=True, text=True, timeout=300)
     assert r.returncode == 2 and "unknown workload" in r.stderr
+
+
+def test_counter_files_are_per_workload():
+    assert bench.traffic_file("kv_up").endswith(os.path.join("profiles", "gemm_kv_up_traffic.json"))
+    assert bench.mfma_file("outlier").endswith(os.path.join("profiles", "gemm_outlier_mfma_busy.json"))
+
+
+def test_cpu_sample_is_bounded():
+    """The CPU baseline's row sample is about 1e11 multiply-adds (a few seconds of the oracle on
+    a GPU machine's host share), a multiple of 64 rows, never more than the workload's rows."""
+    import synth
+    for wl in synth.WORKLOADS.values():
+        r = bench.cpu_sample_rows(wl.M, wl.N, wl.K)
+        assert 1 <= r <= wl.M
+        assert r == wl.M or r * wl.N * wl.K <= bench.CPU_SAMPLE_MACS
+        assert r == wl.M or r % 64 == 0
+    assert bench.cpu_sample_rows(16384, 7168, 7168) == 1920
+
+
+def test_host_cpu_fields():
+    h = bench.host_cpu()
+    assert h["nproc"] >= 1 and h["cpu_count"] >= h["nproc"]

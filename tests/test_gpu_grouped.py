@@ -14,7 +14,8 @@ import torch
 import fp8_act_quant_amd as fq
 import oracle
 import synth
-from helpers import dev_bf16, gemm_check, host_bits16, host_codes, mfma_group_allowance, scale_floor
+from helpers import (check_every_output, dev_bf16, gemm_check, group_allowance_applies, host_bits16, host_codes,
+                     mfma_group_allowance, scale_floor)
 
 pytestmark = pytest.mark.gpu
 
@@ -38,8 +39,9 @@ def quantise_experts(A, W):
 
 
 def allowances(haq, hsa, hwq, hsw, offsets, rows, cols, fp8_products):
-    """Per-output allowance: the scale floor, plus the matrix unit's group truncation for
-    the FP8-product mode, each taken against the weight of the expert owning the row."""
+    """Per-output allowance: the scale floor, plus the matrix unit's group truncation where
+    an explicit FP8-product request has fp32 output, each taken against the weight of the
+    expert owning the row."""
     expert = np.searchsorted(offsets, rows, side="right") - 1
     out = np.zeros(rows.shape, dtype=np.float64)
     for e in np.unique(expert):
@@ -75,8 +77,7 @@ def test_grouped_small_full_output(sizes, N, K, out, mode):
     haq, hsa, hwq, hsw = host_codes(aq), sa.cpu().numpy(), host_codes(wq), sw.cpu().numpy()
     y_hat, bound = oracle.grouped_gemm(haq, hsa, hwq, hsw, offsets)
     rows, cols = np.repeat(np.arange(R), N), np.tile(np.arange(N), R)
-    fp8_products = mode == "fp8" or (mode == "default" and out == "bf16")
-    allow = allowances(haq, hsa, hwq, hsw, offsets, rows, cols, fp8_products).reshape(R, N)
+    allow = allowances(haq, hsa, hwq, hsw, offsets, rows, cols, group_allowance_applies(mode, out)).reshape(R, N)
     res = gemm_check(y_host(y, out), y_hat, bound, out, allow)
     print(f"grouped {sizes} N={N} K={K} {out} {mode}", res, flush=True)
     assert res["violations"] == 0, res
@@ -103,7 +104,7 @@ def test_grouped_maximum_expert_count(E):
     for out, mode in (("bf16", "fp8"), ("f32", "exact")):
         y = fq.fp8_grouped_gemm(aq, sa, wq, sw, off, out_dtype=TORCH_OUT[out], mode=mode)
         torch.cuda.synchronize()
-        allow = allowances(haq, hsa, hwq, hsw, offsets, rows, cols, mode == "fp8").reshape(R, N)
+        allow = allowances(haq, hsa, hwq, hsw, offsets, rows, cols, group_allowance_applies(mode, out)).reshape(R, N)
         res = gemm_check(y_host(y, out), y_hat, bound, out, allow)
         print(f"grouped E={E} {out} {mode}", res, flush=True)
         assert res["violations"] == 0, res
@@ -183,7 +184,9 @@ def test_grouped_k_zero_writes_zeros():
     assert torch.count_nonzero(y).item() == 0
 
 
-def test_grouped_moe_down_full_size_sampled():
+def test_grouped_moe_down_full_size_every_output():
+    """The routed down-projection at full size: every output row of every expert against
+    the oracle's block GEMM with that expert's weight, under the plain bf16 bound."""
     wl = synth.MOE_WORKLOADS["moe_down"]
     A, W, offsets = synth.make_moe_inputs(wl)
     R = int(offsets[-1])
@@ -200,16 +203,16 @@ def test_grouped_moe_down_full_size_sampled():
     assert np.array_equal(host_codes(wq[0]), owq) and np.array_equal(sw[0].cpu().numpy().view(np.uint32),
                                                                      osw.view(np.uint32))
     hwq, hsw = host_codes(wq), sw.cpu().numpy()
-    rows, cols = synth.sample_outputs(R, wl.N, 6144, seed=2)
-    firsts = np.unique(np.concatenate([offsets[:-1], offsets[1:] - 1]).clip(0, R - 1))
-    rows = np.concatenate([rows, np.repeat(firsts, 4)])
-    cols = np.concatenate([cols, np.tile([0, 127, 128, wl.N - 1], len(firsts))])
-    y_hat, bound = oracle.grouped_gemm_sampled(haq, hsa, hwq, hsw, offsets, rows, cols)
-    yh = host_bits16(y)[rows, cols]
-    allow = allowances(haq, hsa, hwq, hsw, offsets, rows, cols, False)
-    res = gemm_check(yh, y_hat, bound, "bf16", allow)
-    print("moe_down", res, flush=True)
-    assert res["violations"] == 0, res
+    checked = 0
+    for e in range(wl.local_experts):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        if r1 == r0:
+            continue
+        res = check_every_output(y[r0:r1], haq[r0:r1], hsa[r0:r1], hwq[e], hsw[e], "bf16", f"moe_down expert {e}",
+                                 chunk_rows=4096)
+        assert res["violations"] == 0 and res["strict_violations"] == 0, (e, res)
+        checked += res["n"]
+    assert checked == R * wl.N
     assert torch.isfinite(y.float()).all()
 
 

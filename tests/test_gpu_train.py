@@ -10,7 +10,8 @@ import torch
 import fp8_act_quant_amd as fq
 import oracle
 import synth
-from helpers import (dev_bf16, gemm_check, host_bits16, host_codes, mfma_group_allowance_rowwise, scale_floor)
+from helpers import (check_every_output, dev_bf16, gemm_check, group_allowance_applies, host_bits16, host_codes,
+                     mfma_group_allowance_rowwise, scale_floor)
 
 pytestmark = pytest.mark.gpu
 
@@ -102,8 +103,8 @@ class RowwiseReference:
         self.fp8 = self.floor + mfma_group_allowance_rowwise(haq, hsa, hbq, hsb, rows, cols).reshape(M, N)
 
     def check(self, y, out, mode):
-        fp8_products = mode == "fp8" or (mode == "default" and out == "bf16")
-        return gemm_check(y_host(y, out), self.y_hat, self.bound, out, self.fp8 if fp8_products else self.floor)
+        return gemm_check(y_host(y, out), self.y_hat, self.bound, out,
+                          self.fp8 if group_allowance_applies(mode, out) else self.floor)
 
 
 def rowwise_check(aq, sa, bq, sb, y, out, mode):
@@ -154,10 +155,10 @@ def test_rowwise_every_tile_configuration(M, N, K):
         fq.lib.fp8q_gemm_force_config(-1, 0)
 
 
-def test_linear_backward_q_down_full_size_sampled():
+def test_linear_backward_q_down_full_size_every_output():
     """Backward of the q down-projection (4096 tokens, 7168 -> 1536) at full size: the
     codes the kernels consumed are the oracle's, dX is checked against the block GEMM through
-    the transposed weight and dW against the per-row GEMM over tokens, on seeded samples."""
+    the transposed weight and dW against the per-row GEMM over tokens, on every output."""
     wl = synth.WORKLOADS["q_down"]
     X, W = synth.make_inputs(wl)
     dY = synth.random_bf16((wl.M, wl.N), seed=101)
@@ -171,21 +172,17 @@ def test_linear_backward_q_down_full_size_sampled():
     # dX = dY . W
     dyq, sdy = oracle.act_quant(dY)
     wqt, swt = oracle.weight_transpose(host_codes(wq), sw.cpu().numpy())
-    rows, cols = synth.sample_outputs(wl.M, wl.K, 4096, seed=3)
-    y_hat, bound = oracle.block_gemm_sampled(dyq, sdy, wqt, swt, rows, cols)
-    res = gemm_check(host_bits16(dx)[rows, cols], y_hat, bound, "bf16", scale_floor(dyq, wqt, rows, cols))
-    print("dX", res, flush=True)
-    assert res["violations"] == 0, res
+    res = check_every_output(dx, dyq, sdy, wqt, swt, "bf16", "dX")
+    assert res["n"] == wl.M * wl.K
+    assert res["violations"] == 0 and res["strict_violations"] == 0, res
     # dW = dY^T . X over tokens (fp32 output: exact slices)
     dyt, sdyt = oracle.act_quant_t(dY)
     xt, sxt = oracle.act_quant_t(X)
     gq, _ = fq.act_quant_t(x)
     assert np.array_equal(host_codes(gq), xt)
-    rows, cols = synth.sample_outputs(wl.N, wl.K, 4096, seed=4)
-    y_hat, bound = oracle.rowwise_gemm_sampled(dyt, sdyt, xt, sxt, rows, cols)
-    res = gemm_check(dw.cpu().numpy()[rows, cols], y_hat, bound, "f32", scale_floor(dyt, xt, rows, cols))
-    print("dW", res, flush=True)
-    assert res["violations"] == 0, res
+    res = check_every_output(dw, dyt, sdyt, xt, sxt, "f32", "dW", rowwise=True)
+    assert res["n"] == wl.N * wl.K
+    assert res["violations"] == 0 and res["strict_violations"] == 0, res
     assert torch.isfinite(dx.float()).all() and torch.isfinite(dw).all()
 
 
