@@ -19,6 +19,8 @@ FP8Q_ERR_ALIGN = 3
 FP8Q_ERR_DTYPE = 4
 FP8Q_ERR_UNSUPPORTED = 5
 FP8Q_ERR_LAUNCH = 6
+FP8Q_ERR_WORKSPACE = 7
+FP8Q_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 FP8Q_OUT_F32 = 0
 FP8Q_OUT_BF16 = 1
@@ -39,6 +41,7 @@ SIGNATURES = {
     "fp8_block_gemm_bias": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.c_int, _I64, _I64, _I64, _P,
                                            ctypes.c_size_t, _P]),
     "fp8_block_gemm_workspace_bytes": (ctypes.c_size_t, [_I64, _I64, _I64, ctypes.c_int]),
+    "fp8_block_gemm_noalloc": (ctypes.c_int, [_P, _P, _P, _P, _P, ctypes.c_int, _I64, _I64, _I64, _P]),
     "fp8_grouped_gemm": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.c_int, _I64, _I64, _I64, _I64, _P]),
     "fp8_act_quant_t": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _P]),
     "fp8_weight_transpose": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _P]),

@@ -133,6 +133,33 @@ int fp8_block_gemm_bias(const uint8_t *aq, const float *sa, const uint8_t *wq, c
                                           K, workspace, workspace_bytes, static_cast<hipStream_t>(stream)));
 }
 
+int fp8_block_gemm_noalloc(const uint8_t *aq, const float *sa, const uint8_t *wq, const float *sw, void *y,
+                           int y_dtype, int64_t M, int64_t N, int64_t K, void *stream) {
+    static_assert(FP8Q_NOALLOC_SCRATCH_BYTES == fp8q::kNoallocScratchBytes, "scratch size in the header");
+    const int dtype = y_dtype & 0xFF;
+    const bool sa_kmajor = (y_dtype & FP8Q_SA_KMAJOR) != 0;
+    const int mode = y_dtype & ~0xFF & ~FP8Q_SA_KMAJOR;
+    if (dtype != FP8Q_OUT_F32 && dtype != FP8Q_OUT_BF16) return FP8Q_ERR_DTYPE;
+    if (mode != 0 && mode != FP8Q_GEMM_FP8_PRODUCTS && mode != FP8Q_GEMM_EXACT_SLICES) return FP8Q_ERR_DTYPE;
+    if (int e = shape_ok(M, K)) return e;
+    if (int e = shape_ok(N, K)) return e;
+    if (M > 0 && N > kMaxElems / M) return FP8Q_ERR_SHAPE;
+    if (K > kMaxGemmK) return FP8Q_ERR_SHAPE;
+    if (sa_kmajor && K > 0 && M >= kMaxKmajorScales / (K / kBlock)) return FP8Q_ERR_SHAPE;
+    if (M == 0 || N == 0) return FP8Q_OK;
+    const bool exact = mode == FP8Q_GEMM_EXACT_SLICES || (mode == 0 && dtype == FP8Q_OUT_F32);
+    // the split-K plan fp8_block_gemm would use with its full workspace must fit the static scratch
+    if (K > 0 && fp8q::gemm_workspace_bytes(M, N, K, dtype == FP8Q_OUT_BF16, exact) > FP8Q_NOALLOC_SCRATCH_BYTES)
+        return FP8Q_ERR_WORKSPACE;
+    if (!y) return FP8Q_ERR_NULL;
+    if (K > 0 && (!aq || !sa || !wq || !sw)) return FP8Q_ERR_NULL;
+    if (misaligned(aq, 16) || misaligned(wq, 16) || misaligned(y, 16) || misaligned(sa, 4) || misaligned(sw, 4))
+        return FP8Q_ERR_ALIGN;
+    if (int e = check_device()) return e;
+    return finish(fp8q::launch_block_gemm_noalloc(aq, sa, wq, sw, y, dtype == FP8Q_OUT_BF16, exact, sa_kmajor, M, N,
+                                                  K, static_cast<hipStream_t>(stream)));
+}
+
 int fp8_grouped_gemm(const uint8_t *aq, const float *sa, const uint8_t *wq, const float *sw, const int64_t *offsets,
                      void *y, int y_dtype, int64_t experts, int64_t rows, int64_t N, int64_t K, void *stream) {
     const int dtype = y_dtype & 0xFF;
@@ -240,10 +267,13 @@ const char *fp8q_strerror(int status) {
     case FP8Q_ERR_DTYPE: return "unknown output dtype";
     case FP8Q_ERR_UNSUPPORTED: return "no gfx950 device is current";
     case FP8Q_ERR_LAUNCH: return "kernel launch failed";
+    case FP8Q_ERR_WORKSPACE:
+        return "the shape's split-K schedule needs more scratch than the static scratch holds "
+               "(FP8Q_NOALLOC_SCRATCH_BYTES); call fp8_block_gemm with a workspace instead";
     default: return "unknown status";
     }
 }
 
-int fp8q_version(void) { return (1 << 16) | 2; }
+int fp8q_version(void) { return (1 << 16) | 3; }
 
 }  // extern "C"

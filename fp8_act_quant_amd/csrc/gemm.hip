@@ -1162,6 +1162,47 @@ size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, bool, bool exact, b
     return split_bytes(make_plan(M, N, K, exact, 0, true, rowb));
 }
 
+// Split-K scratch of launch_block_gemm_noalloc, for callers that cannot allocate: one array
+// per GPU, allocated with the library's code object when it is loaded on that GPU and held
+// until the process ends. Host code never passes `scratch` itself to a kernel (on the host it
+// is only a stand-in for the symbol): the device address of each GPU's copy is looked up once
+// per device with hipGetSymbolAddress and kept in g_scratch_addr.
+static __device__ __align__(256) uint8_t scratch[kNoallocScratchBytes];
+
+constexpr int kScratchDevices = 64;
+static std::atomic<void *> g_scratch_addr[kScratchDevices];
+
+// Device address of the current device's scratch (looked up on the device's first call).
+static hipError_t current_scratch(void **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+    void *p = g_scratch_addr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        // racing first calls on one device look up the same address; either store is correct
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        g_scratch_addr[dev].store(p, std::memory_order_release);
+    }
+    *out = p;
+    return hipSuccess;
+}
+
+hipError_t launch_block_gemm_noalloc(const uint8_t *aq, const float *sa, const uint8_t *wq, const float *sw, void *y,
+                                     bool out_bf16, bool exact, bool sa_kmajor, int64_t M, int64_t N, int64_t K,
+                                     hipStream_t stream) {
+    if (M == 0 || N == 0) return hipSuccess;
+    // the caller has checked that this shape's split-K plan fits the scratch; with that
+    // capacity make_plan picks the same plan as launch_block_gemm given the full workspace
+    if (gemm_workspace_bytes(M, N, K, out_bf16, exact) > kNoallocScratchBytes) return hipErrorInvalidValue;
+    void *ws = nullptr;
+    const hipError_t e = current_scratch(&ws);
+    if (e != hipSuccess) return e;
+    return launch_block_gemm(aq, sa, wq, sw, nullptr, y, out_bf16, exact, sa_kmajor, M, N, K, ws,
+                             kNoallocScratchBytes, stream);
+}
 
 template <int BM, int BN, int NW, int WAVES_M, int NSTAGE, int EXACT, int GROUPED = 0, int ROWB = 0>
 static hipError_t launch_cfg(GemmArgs a, bool out_bf16, int splits, hipStream_t stream) {

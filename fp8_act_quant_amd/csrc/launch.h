@@ -27,6 +27,14 @@ hipError_t launch_block_gemm(const uint8_t *aq, const float *sa, const uint8_t *
                              int64_t N, int64_t K, void *workspace, size_t workspace_bytes, hipStream_t stream);
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, bool out_bf16, bool exact, bool rowb = false);
 
+// launch_block_gemm (no bias) with the library's static per-GPU split-K scratch of
+// kNoallocScratchBytes instead of a caller's workspace; allocates nothing. The shape's
+// gemm_workspace_bytes must not exceed kNoallocScratchBytes (hipErrorInvalidValue otherwise).
+// Calls on one GPU share that scratch, so calls that overlap on one GPU race.
+constexpr size_t kNoallocScratchBytes = (size_t)32 << 20;
+hipError_t launch_block_gemm_noalloc(const uint8_t *aq, const float *sa, const uint8_t *wq, const float *sw, void *y,
+                                     bool out_bf16, bool exact, bool sa_kmajor, int64_t M, int64_t N, int64_t K,
+                                     hipStream_t stream);
 
 // GEMM with per-row scales on both operands: Y = sum over slices kb of
 // (sum_k aq[m,k] bq[n,k]) * sa[m,kb] * sb[n,kb], sb [N, K/128]. Otherwise as launch_block_gemm

@@ -59,6 +59,7 @@ extern "C" {
 #define FP8Q_ERR_DTYPE 4       /* unknown output dtype                                      */
 #define FP8Q_ERR_UNSUPPORTED 5 /* no gfx950 device is current                               */
 #define FP8Q_ERR_LAUNCH 6      /* the kernel launch failed                                  */
+#define FP8Q_ERR_WORKSPACE 7   /* more scratch needed than fp8_block_gemm_noalloc holds     */
 
 /* Output dtypes of fp8_block_gemm (low 8 bits of its y_dtype argument). */
 #define FP8Q_OUT_F32 0
@@ -161,6 +162,24 @@ int fp8_block_gemm(const uint8_t *aq, const float *sa, const uint8_t *wq, const 
 int fp8_block_gemm_bias(const uint8_t *aq, const float *sa, const uint8_t *wq, const float *sw,
                         const float *bias, void *y, int y_dtype, int64_t M, int64_t N, int64_t K,
                         void *workspace, size_t workspace_bytes, void *stream);
+
+/* fp8_block_gemm_noalloc -- fp8_block_gemm for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc). It
+ * calls no allocating routine; in place of the workspace argument it uses a static split-K
+ * scratch of FP8Q_NOALLOC_SCRATCH_BYTES (32 MiB) per GPU, which the library holds on every
+ * GPU it is loaded on until the process ends.
+ *   Arguments, layouts, modes (y_dtype), alignment and results: as fp8_block_gemm, whose
+ *   tile and split-K plan it uses, so its output is bit-identical to fp8_block_gemm's with a
+ *   workspace of fp8_block_gemm_workspace_bytes() bytes.
+ *   Returns FP8Q_ERR_WORKSPACE, enqueueing nothing, when fp8_block_gemm_workspace_bytes()
+ *   for the shape and y_dtype exceeds FP8Q_NOALLOC_SCRATCH_BYTES.
+ *   The scratch needs no clearing (its split-K arrival words are tagged per launch) and keeps
+ *   the last call's contents. Every call on one GPU shares that GPU's scratch: calls that may
+ *   overlap on one GPU (other streams, other host threads) race and must be serialised by the
+ *   caller. */
+#define FP8Q_NOALLOC_SCRATCH_BYTES ((size_t)33554432)
+int fp8_block_gemm_noalloc(const uint8_t *aq, const float *sa, const uint8_t *wq, const float *sw,
+                           void *y, int y_dtype, int64_t M, int64_t N, int64_t K, void *stream);
 
 /* fp8_grouped_gemm -- the block-scaled GEMMs of several experts in one launch, for the
  * routed experts of a mixture-of-experts layer: expert e multiplies its own rows of A by its
