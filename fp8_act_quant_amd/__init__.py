@@ -24,7 +24,7 @@ BLOCK = 128
 __all__ = [
     "BLOCK", "Fp8qError", "act_quant", "weight_quant", "weight_dequant", "fp8_gemm", "fp8_grouped_gemm",
     "linear", "gemm_workspace_bytes", "lib", "act_quant_t", "weight_transpose", "fp8_gemm_rowwise",
-    "linear_backward",
+    "linear_backward", "bf16_gemm",
 ]
 
 
@@ -275,25 +275,68 @@ def fp8_grouped_gemm(a: torch.Tensor, a_s: torch.Tensor, w: torch.Tensor, w_s: t
     return out
 
 
+def bf16_gemm(x: torch.Tensor, w: torch.Tensor, bias: torch.Tensor | None = None,
+              out_dtype=torch.bfloat16, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Y = x . w^T (+ bias) on bf16 operands, fp32 accumulation: the bf16 GEMM of linear()'s
+    bf16 branch. x: bfloat16 [..., K]; w: bfloat16 [N, K] (K a multiple of 64); bias:
+    optional [N], added in fp32 before the output rounding. Returns [..., N] in out_dtype
+    (torch.bfloat16 or torch.float32)."""
+    _need(x, "x", torch.bfloat16)
+    _need(w, "w", torch.bfloat16)
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("out_dtype must be torch.float32 or torch.bfloat16")
+    K = x.shape[-1]
+    if w.dim() != 2 or w.shape[1] != K:
+        raise ValueError("w must be [N, K] with the activation's K")
+    if K % 64:
+        raise ValueError("K must be a multiple of 64")
+    N = w.shape[0]
+    M = math.prod(x.shape[:-1])
+    shape = (*x.shape[:-1], N)
+    if out is None:
+        out = torch.empty(shape, dtype=out_dtype, device=x.device)
+    else:
+        _need(out, "out", out_dtype, align=4)
+        if tuple(out.shape) != shape:
+            raise ValueError(f"out must be {shape}")
+    b_ptr = None
+    if bias is not None:
+        if not isinstance(bias, torch.Tensor) or bias.device != x.device or tuple(bias.shape) != (N,):
+            raise ValueError(f"bias must be a [{N}] tensor on {x.device}")
+        bias = bias.to(torch.float32).contiguous()
+        b_ptr = bias.data_ptr()
+    code = FP8Q_OUT_BF16 if out_dtype == torch.bfloat16 else FP8Q_OUT_F32
+    with torch.cuda.device(x.device):
+        check("fp8_bf16_gemm", lib.fp8_bf16_gemm(x.data_ptr(), w.data_ptr(), b_ptr, out.data_ptr(), code, M, N, K,
+                                                 _stream(x)))
+    return out
+
+
 def linear(x: torch.Tensor, weight: torch.Tensor, bias: torch.Tensor | None = None,
            weight_scale: torch.Tensor | None = None, gemm_impl: str = "fp8",
            out_dtype=torch.bfloat16) -> torch.Tensor:
-    """The linear() dispatch of the pomoai.com "DeepSeek-V3" page (FP8 mixed-precision
-    training section): a weight stored in more than one byte per element is applied as is
-    (torch's linear); with gemm_impl == "bf16" the FP8 weight is dequantised with
-    weight_dequant and applied by torch's linear; otherwise x is quantised with act_quant
-    and multiplied by fp8_gemm, with the bias added in the GEMM's epilogue.
+    """y = x . weight^T (+ bias) for bf16 activations x [..., K], as the pomoai.com
+    "DeepSeek-V3" page's linear() describes it (FP8 mixed-precision training section), with
+    every product in this library's kernels:
 
-    x: bf16 [..., K]; weight: [N, K] (float8_e4m3fn with weight_scale
-    [ceil(N/128), K/128], or a wider dtype); bias: optional [N]."""
-    if weight.element_size() > 1:
-        return torch.nn.functional.linear(x, weight, bias)
+    * a weight stored unquantised (bfloat16 [N, K]) goes through the bf16 GEMM;
+    * an FP8 weight (float8_e4m3fn [N, K] with weight_scale [ceil(N/128), K/128]) with
+      gemm_impl "bf16" is dequantised by weight_dequant and then goes through the bf16 GEMM;
+    * an FP8 weight with gemm_impl "fp8" (the default): x is quantised by act_quant
+      (K-block-major scales) and multiplied by the block-scaled GEMM, the bias added in its
+      epilogue.
+
+    Other weight dtypes are rejected. bias: optional [N]."""
+    if gemm_impl not in ("fp8", "bf16"):
+        raise ValueError('gemm_impl must be "fp8" or "bf16"')
+    if weight.dtype == torch.bfloat16:
+        return bf16_gemm(x, weight, bias, out_dtype=out_dtype)
+    if weight.dtype != torch.float8_e4m3fn:
+        raise TypeError(f"weight must be torch.float8_e4m3fn (with weight_scale) or torch.bfloat16, got {weight.dtype}")
     if weight_scale is None:
         raise ValueError("an FP8 weight needs its weight_scale")
     if gemm_impl == "bf16":
-        return torch.nn.functional.linear(x, weight_dequant(weight, weight_scale), bias)
-    if gemm_impl != "fp8":
-        raise ValueError('gemm_impl must be "fp8" or "bf16"')
+        return bf16_gemm(x, weight_dequant(weight, weight_scale), bias, out_dtype=out_dtype)
     # K-block-major scales: the GEMM fetches each K slice's scales as whole cache lines
     M, nkb = math.prod(x.shape[:-1]), x.shape[-1] // BLOCK
     q, s = act_quant(x, scale_layout="kmajor" if M * nkb < MAX_KMAJOR_SCALES else "row")

@@ -25,6 +25,10 @@ constexpr int64_t kMaxGemmK = ((int64_t)1 << 24) - 128;
 constexpr int64_t kMaxGridX = 0x7FFFFFFF, kMaxGridY = 65535;
 // a grid dimension counts at most 2^32 - 1 work-items: workgroups of 256 threads along it
 constexpr int64_t kMaxBlocks256 = 0xFFFFFFFFll / 256;
+// The bf16 GEMM advances K in steps of 64 elements and addresses a workgroup's rows (at most
+// 256 of 2K bytes) through 32-bit buffer resources: K < 2^23.
+constexpr int64_t kBf16Step = 64;
+constexpr int64_t kMaxBf16K = ((int64_t)1 << 23) - kBf16Step;
 // K-block-major activation scales are addressed with 32-bit byte offsets: M * K/128 < 2^29
 constexpr int64_t kMaxKmajorScales = (int64_t)1 << 29;
 
@@ -131,6 +135,19 @@ int fp8_block_gemm_bias(const uint8_t *aq, const float *sa, const uint8_t *wq, c
     const bool exact = mode == FP8Q_GEMM_EXACT_SLICES || (mode == 0 && dtype == FP8Q_OUT_F32);
     return finish(fp8q::launch_block_gemm(aq, sa, wq, sw, bias, y, dtype == FP8Q_OUT_BF16, exact, sa_kmajor, M, N,
                                           K, workspace, workspace_bytes, static_cast<hipStream_t>(stream)));
+}
+
+int fp8_bf16_gemm(const uint16_t *x, const uint16_t *w, const float *bias, void *y, int y_dtype, int64_t M,
+                  int64_t N, int64_t K, void *stream) {
+    if (y_dtype != FP8Q_OUT_F32 && y_dtype != FP8Q_OUT_BF16) return FP8Q_ERR_DTYPE;
+    if (M < 0 || N < 0 || K < 0 || (K % kBf16Step) != 0 || K > kMaxBf16K) return FP8Q_ERR_SHAPE;
+    if ((K > 0 && (M > kMaxElems / K || N > kMaxElems / K)) || (M > 0 && N > kMaxElems / M)) return FP8Q_ERR_SHAPE;
+    if (M == 0 || N == 0) return FP8Q_OK;
+    if (!y || (K > 0 && (!x || !w))) return FP8Q_ERR_NULL;
+    if (misaligned(x, 16) || misaligned(w, 16) || misaligned(y, 4) || misaligned(bias, 4)) return FP8Q_ERR_ALIGN;
+    if (int e = check_device()) return e;
+    return finish(fp8q::launch_bf16_gemm(x, w, bias, y, y_dtype == FP8Q_OUT_BF16, M, N, K,
+                                         static_cast<hipStream_t>(stream)));
 }
 
 int fp8_block_gemm_noalloc(const uint8_t *aq, const float *sa, const uint8_t *wq, const float *sw, void *y,
@@ -274,6 +291,6 @@ const char *fp8q_strerror(int status) {
     }
 }
 
-int fp8q_version(void) { return (1 << 16) | 3; }
+int fp8q_version(void) { return (1 << 16) | 4; }
 
 }  // extern "C"

@@ -36,6 +36,12 @@ hipError_t launch_block_gemm_noalloc(const uint8_t *aq, const float *sa, const u
                                      bool out_bf16, bool exact, bool sa_kmajor, int64_t M, int64_t N, int64_t K,
                                      hipStream_t stream);
 
+// Y = X . W^T on bf16 operands (the bf16 branch of linear()): x [M, K], w [N, K] bf16
+// bits, fp32 accumulation, optional fp32 bias [N], Y fp32 or bf16 (RNE). K a multiple of 64
+// below 2^23.
+hipError_t launch_bf16_gemm(const uint16_t *x, const uint16_t *w, const float *bias, void *y, bool out_bf16, int64_t M,
+                            int64_t N, int64_t K, hipStream_t stream);
+
 // GEMM with per-row scales on both operands: Y = sum over slices kb of
 // (sum_k aq[m,k] bq[n,k]) * sa[m,kb] * sb[n,kb], sb [N, K/128]. Otherwise as launch_block_gemm
 // (no bias); its workspace size is gemm_workspace_bytes(..., rowb = true).

@@ -163,6 +163,23 @@ int fp8_block_gemm_bias(const uint8_t *aq, const float *sa, const uint8_t *wq, c
                         const float *bias, void *y, int y_dtype, int64_t M, int64_t N, int64_t K,
                         void *workspace, size_t workspace_bytes, void *stream);
 
+/* fp8_bf16_gemm -- Y = X . W^T on bf16 operands: the bf16 branch of linear().
+ * (pomoai.com "DeepSeek-V3", the linear() listing in section "FP8 mixed-precision
+ * training": when the GEMM is not done in FP8, the weight is dequantised to bf16 by
+ * weight_dequant and the layer is a plain bf16 linear, y = x . W^T, plus the bias.)
+ *   x  [M, K] bf16 (bit patterns).              16-byte aligned.
+ *   w  [N, K] bf16, e.g. from fp8_weight_dequant. 16-byte aligned.
+ *   bias [N] fp32 or NULL; added to the fp32 accumulator before the output rounding.
+ *                                               4-byte aligned.
+ *   y  [M, N]: fp32 (y_dtype = FP8Q_OUT_F32) or bf16 bits (FP8Q_OUT_BF16, RNE of the fp32
+ *      accumulator).                            4-byte aligned.
+ *   Every product is exact in fp32; the products are summed in fp32 by the bf16 matrix
+ *   unit, 32 at a time, the partial sums chained in fp32 along K. M, N >= 0 arbitrary
+ *   (ragged tails masked); K a multiple of 64 below 2^23 (FP8Q_ERR_SHAPE otherwise). With
+ *   K = 0 the output is the bias (or zeros). */
+int fp8_bf16_gemm(const uint16_t *x, const uint16_t *w, const float *bias, void *y, int y_dtype,
+                  int64_t M, int64_t N, int64_t K, void *stream);
+
 /* fp8_block_gemm_noalloc -- fp8_block_gemm for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc). It
  * calls no allocating routine; in place of the workspace argument it uses a static split-K

@@ -59,6 +59,7 @@ def _load():
         "or_block_gemm": (None, [P, P, P, P, I64, I64, I64, P, P]),
         "or_block_gemm_sampled": (None, [P, P, P, P, I64, I64, I64, P, P, I64, P, P]),
         "or_matmul_bf16_sampled": (None, [P, P, I64, P, P, I64, P]),
+        "or_matmul_bf16": (None, [P, P, I64, I64, I64, P, P]),
         "or_rowwise_gemm": (None, [P, P, P, P, I64, I64, I64, P, P]),
         "or_rowwise_gemm_sampled": (None, [P, P, P, P, I64, P, P, I64, P, P]),
         "or_e4m3_encode_batch": (None, [P, P, I64]),
@@ -291,6 +292,22 @@ def rowwise_gemm_sampled(aq, sa, bq, sb, rows, cols):
     b = np.empty(rows.shape, dtype=np.float64)
     _load().or_rowwise_gemm_sampled(_ptr(aq), _ptr(sa), _ptr(bq), _ptr(sb), K, _ptr(rows), _ptr(cols), rows.size,
                                     _ptr(y), _ptr(b))
+    return y, b
+
+
+def matmul_bf16(x_bf16, w_bf16):
+    """The bf16 linear of the linear() listing's bf16 branch, y = x . w^T over bf16 values
+    (x [M, K], w [N, K] as uint16 bit patterns), in float64: (y [M, N], bound [M, N]) with
+    bound = sum_k |x_k w_k|."""
+    x = _c(x_bf16, np.uint16)
+    w = _c(w_bf16, np.uint16)
+    M, K = x.shape
+    N, K2 = w.shape
+    if K != K2:
+        raise ValueError("K mismatch")
+    y = np.empty((M, N), dtype=np.float64)
+    b = np.empty((M, N), dtype=np.float64)
+    _load().or_matmul_bf16(_ptr(x), _ptr(w), M, N, K, _ptr(y), _ptr(b))
     return y, b
 
 

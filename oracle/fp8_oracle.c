@@ -362,6 +362,35 @@ void or_rowwise_gemm_sampled(const uint8_t *aq, const float *sa, const uint8_t *
         rowwise_one(dec, aq, sa, bq, sb, K, rows[i], cols[i], y + i, bound + i);
 }
 
+/* ---------------------------------------------------------------------------------
+ * bf16 linear (the linear() listing's bf16 branch, [P5]: the FP8 weight is dequantised by
+ * weight_dequant and the layer is a plain bf16 linear y = x . W^T):
+ *   y[m, n]     = sum_k x[m, k] * w[n, k]
+ *   bound[m, n] = sum_k |x[m, k] * w[n, k]|
+ * over the bf16 values (x and the dequantised w), in float64. Each bf16 x bf16 product is
+ * exact in float64 (16 significant bits); the float64 sum rounds at ~2^-53 relative to
+ * the bound, far below the fp32 accumulation it checks.
+ * ------------------------------------------------------------------------------- */
+void or_matmul_bf16(const uint16_t *x, const uint16_t *w, int64_t M, int64_t N, int64_t K, double *y,
+                    double *bound)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t m = 0; m < M; ++m) {
+        const uint16_t *xr = x + m * K;
+        for (int64_t n = 0; n < N; ++n) {
+            const uint16_t *wr = w + n * K;
+            double acc = 0.0, b = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                double t = (double)or_bf16_to_f32(xr[k]) * (double)or_bf16_to_f32(wr[k]);
+                acc += t;
+                b += fabs(t);
+            }
+            y[m * N + n] = acc;
+            bound[m * N + n] = b;
+        }
+    }
+}
+
 /* Unquantised float64 product of the original bf16 operands at sampled outputs, for the
  * informational relative error of the FP8 path: y[i] = sum_k x[r,k] * w[c,k]. */
 void or_matmul_bf16_sampled(const uint16_t *x, const uint16_t *w, int64_t K, const int64_t *rows,

@@ -66,19 +66,21 @@ def ulp_bf16(v: np.ndarray) -> np.ndarray:
     return np.exp2(np.maximum(e - 7, -133))
 
 
-def gemm_check(y: np.ndarray, y_hat: np.ndarray, bound: np.ndarray, out: str, allowance=None) -> dict:
+def gemm_check(y: np.ndarray, y_hat: np.ndarray, bound: np.ndarray, out: str, allowance=None,
+               rel: float = 1e-5) -> dict:
     """y: fp32 values (out == 'f32') or bf16 bit patterns (out == 'bf16').
     Returns counts; 'violations' must be 0. `allowance` (per element, optional) is the
     matrix-unit allowance added to the bound; 'strict_violations' counts elements outside
-    the plain bound."""
+    the plain bound. `rel` is the bound's factor on sum |a w| (1e-5 for the block-scaled
+    GEMM)."""
     y_hat = np.asarray(y_hat, dtype=np.float64)
     bound = np.asarray(bound, dtype=np.float64)
     allow = np.zeros_like(y_hat) if allowance is None else np.asarray(allowance, dtype=np.float64)
     if out == "f32":
         yv = np.asarray(y, dtype=np.float32).astype(np.float64)
         err = np.abs(yv - y_hat)
-        strict = ~(err <= 1e-5 * bound)
-        bad = ~(err <= 1e-5 * bound + allow)
+        strict = ~(err <= rel * bound)
+        bad = ~(err <= rel * bound + allow)
         ratio = err / np.maximum(bound, 1e-300)
         return {"n": int(y_hat.size), "violations": int(bad.sum()), "strict_violations": int(strict.sum()),
                 "max_err_over_bound": float(ratio.max(initial=0))}
@@ -88,8 +90,8 @@ def gemm_check(y: np.ndarray, y_hat: np.ndarray, bound: np.ndarray, out: str, al
     within_ulp = dist <= 1
     yv = oracle.bf16_to_f32_array(yb).astype(np.float64)
     err = np.abs(yv - y_hat)
-    fallback = err <= 1e-5 * bound + ulp_bf16(y_hat)
-    bad = ~(within_ulp | fallback | (err <= 1e-5 * bound + ulp_bf16(y_hat) + allow))
+    fallback = err <= rel * bound + ulp_bf16(y_hat)
+    bad = ~(within_ulp | fallback | (err <= rel * bound + ulp_bf16(y_hat) + allow))
     return {"n": int(y_hat.size), "violations": int(bad.sum()),
             "strict_violations": int((~(within_ulp | fallback)).sum()),
             "beyond_1ulp_accepted": int((~within_ulp & fallback).sum()),
@@ -207,4 +209,38 @@ def check_every_output(y_dev, haq, hsa, hwq, hsw, out: str, label: str, chunk_ro
             for k, v in res.items():
                 total[k] = max(total[k], v) if k.startswith("max") else total[k] + v
         print(f"{label} rows {r0}..{r1 - 1}: {res}", flush=True)
+    return total
+
+
+def bf16_linear_rel(K: int) -> float:
+    """Bound factor of the bf16 GEMM (fp32 accumulation of exact bf16 products): one fp32
+    rounding of the running sum per 32-product matrix-unit step along K, plus one, each at
+    most 2^-24 of sum |x w| (the products themselves are exact)."""
+    return (K // 32 + 1) * 2.0 ** -24
+
+
+def check_bf16_linear_every_output(y_dev, x_bits: np.ndarray, w_bits: np.ndarray, out: str, label: str,
+                                   bias: np.ndarray | None = None, chunk_rows: int = 1024) -> dict:
+    """Every output of a bf16 GEMM result on the device against the oracle's float64 bf16
+    linear (+ bias in float64, with one extra fp32 rounding of the addition allowed: it is
+    counted in 'violations', not in 'strict_violations'), in row chunks."""
+    M, K = x_bits.shape
+    rel = bf16_linear_rel(K)
+    total = None
+    for r0 in range(0, M, chunk_rows):
+        r1 = min(r0 + chunk_rows, M)
+        y_hat, bound = oracle.matmul_bf16(x_bits[r0:r1], w_bits)
+        allow = None
+        if bias is not None:
+            y_hat = y_hat + bias.astype(np.float64)[None, :]
+            allow = 2.0 ** -23 * np.abs(y_hat)
+        yc = y_dev[r0:r1]
+        yh = yc.float().cpu().numpy() if out == "f32" else host_bits16(yc)
+        res = gemm_check(yh, y_hat, bound, out, allow, rel=rel)
+        if total is None:
+            total = res
+        else:
+            for k, v in res.items():
+                total[k] = max(total[k], v) if k.startswith("max") else total[k] + v
+    print(f"{label}: {total}", flush=True)
     return total

@@ -1,0 +1,118 @@
+"""GPU parity of the bf16 GEMM (the bf16 branch of linear(): the FP8 weight dequantised by
+weight_dequant, then a plain bf16 linear) against the oracle's float64 bf16 linear, through
+the C ABI. Tolerance (tests/helpers.py, bf16_linear_rel): every product is exact in fp32 and
+the matrix unit sums them in fp32 32 at a time, so |y - y_hat| <= (K/32 + 1) 2^-24 sum |x w|
+for fp32 output; bf16 output within 1 ulp of RN(y_hat), or within that bound plus one ulp
+near cancellation."""
+import numpy as np
+import pytest
+import torch
+
+import fp8_act_quant_amd as fq
+import oracle
+import synth
+from helpers import bf16_linear_rel, check_bf16_linear_every_output, dev_bf16, host_bits16, host_codes
+
+pytestmark = pytest.mark.gpu
+
+TORCH_OUT = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+@pytest.mark.parametrize("with_bias", [False, True])
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+@pytest.mark.parametrize("M,N,K", [(1, 1, 64), (37, 200, 384), (300, 576, 256), (256, 128, 64), (513, 129, 1024),
+                                   (260, 1000, 1536)])
+def test_bf16_gemm_small_every_output(M, N, K, out, with_bias):
+    X = synth.random_bf16((M, K), seed=M + 3 * N + K)
+    W = synth.random_bf16((N, K), seed=5 * M + N + K, std=0.02)
+    bias = np.random.Generator(np.random.PCG64(N + 1)).standard_normal(N).astype(np.float32) if with_bias else None
+    y = fq.bf16_gemm(dev_bf16(X), dev_bf16(W), None if bias is None else torch.from_numpy(bias).cuda(),
+                     out_dtype=TORCH_OUT[out])
+    torch.cuda.synchronize()
+    res = check_bf16_linear_every_output(y, X, W, out, f"bf16 gemm {M}x{N}x{K} {out} bias={with_bias}", bias)
+    assert res["n"] == M * N
+    # (with a bias, the one fp32 rounding of the addition is part of the bound: violations)
+    assert res["violations"] == 0 and (with_bias or res["strict_violations"] == 0), res
+
+
+def test_bf16_gemm_k_zero_is_bias_and_empty_m():
+    x = torch.empty((5, 0), dtype=torch.bfloat16, device="cuda")
+    w = torch.empty((7, 0), dtype=torch.bfloat16, device="cuda")
+    b = torch.arange(7, dtype=torch.float32, device="cuda")
+    y = fq.bf16_gemm(x, w, b, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(y, b.expand(5, 7))
+    assert fq.bf16_gemm(torch.empty((0, 64), dtype=torch.bfloat16, device="cuda"),
+                        torch.zeros((3, 64), dtype=torch.bfloat16, device="cuda")).shape == (0, 3)
+
+
+@pytest.mark.parametrize("name", ["q_down", "kv_down"])
+def test_linear_bf16_branch_full_size_every_output(name):
+    """linear(gemm_impl="bf16") at the projection's full size: the weight quantised and
+    dequantised by the library (bit-exact with the oracle's weight_dequant), then every output
+    of the bf16 GEMM (bf16 output, with a bias) against the oracle's bf16 linear."""
+    wl = synth.WORKLOADS[name]
+    X, W = synth.make_inputs(wl)
+    print(f"linear bf16 branch {name} M={wl.M} N={wl.N} K={wl.K}", flush=True)
+    bias = np.random.Generator(np.random.PCG64(3)).standard_normal(wl.N).astype(np.float32)
+    x = dev_bf16(X)
+    wq, sw = fq.weight_quant(dev_bf16(W))
+    y = fq.linear(x, wq, torch.from_numpy(bias).cuda(), weight_scale=sw, gemm_impl="bf16")
+    torch.cuda.synchronize()
+    assert y.dtype == torch.bfloat16 and y.shape == (wl.M, wl.N)
+    wd = oracle.weight_dequant(host_codes(wq), sw.cpu().numpy())
+    assert np.array_equal(host_bits16(fq.weight_dequant(wq, sw)), wd)
+    res = check_bf16_linear_every_output(y, X, wd, "bf16", f"linear bf16 {name}", bias)
+    assert res["n"] == wl.M * wl.N
+    assert res["violations"] == 0, res
+
+
+def test_linear_dispatch():
+    """linear(): an FP8 weight with gemm_impl "fp8" is act_quant + the block GEMM with the bias
+    fused; with gemm_impl "bf16" it is weight_dequant + the bf16 GEMM; a bf16 weight goes to the
+    bf16 GEMM as it is; other weight dtypes, and an FP8 weight without its scale, are rejected."""
+    M, N, K = 37, 300, 512
+    x = dev_bf16(synth.random_bf16((M, K), seed=41))
+    Wb = dev_bf16(synth.random_bf16((N, K), seed=42, std=0.02))
+    bias = dev_bf16(synth.random_bf16((N,), seed=43))
+    wq, sw = fq.weight_quant(Wb)
+    q, s = fq.act_quant(x, scale_layout="kmajor")
+    ref_fp8 = fq.fp8_gemm(q, s, wq, sw, out_dtype=torch.bfloat16, bias=bias)
+    assert torch.equal(fq.linear(x, wq, bias, weight_scale=sw).view(torch.int16), ref_fp8.view(torch.int16))
+    ref_bf16 = fq.bf16_gemm(x, fq.weight_dequant(wq, sw), bias)
+    assert torch.equal(fq.linear(x, wq, bias, weight_scale=sw, gemm_impl="bf16").view(torch.int16),
+                       ref_bf16.view(torch.int16))
+    assert torch.equal(fq.linear(x, Wb, bias).view(torch.int16), fq.bf16_gemm(x, Wb, bias).view(torch.int16))
+    # the bf16 branch against the oracle on every output
+    res = check_bf16_linear_every_output(fq.linear(x, Wb, bias), host_bits16(x), host_bits16(Wb), "bf16",
+                                         "linear bf16 weight", oracle.bf16_to_f32_array(host_bits16(bias)))
+    assert res["violations"] == 0, res
+    with pytest.raises(TypeError):
+        fq.linear(x, Wb.float(), bias)
+    with pytest.raises(ValueError):
+        fq.linear(x, wq, bias)   # FP8 weight without its scale
+    with pytest.raises(ValueError):
+        fq.linear(x, wq, bias, weight_scale=sw, gemm_impl="fp16")
+    with pytest.raises(ValueError):
+        fq.fp8_gemm(q, s, wq, sw, bias=bias[:-1])
+
+
+def test_bf16_gemm_deterministic_and_error_paths():
+    from fp8_act_quant_amd import _lib as L
+    X = dev_bf16(synth.random_bf16((700, 1024), 51))
+    W = dev_bf16(synth.random_bf16((300, 1024), 52, std=0.02))
+    y1 = fq.bf16_gemm(X, W)
+    y2 = fq.bf16_gemm(X, W)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    g = fq.lib.fp8_bf16_gemm
+    p = X.data_ptr()
+    y = torch.empty((4, 4), dtype=torch.float32, device="cuda")
+    assert g(p, p, None, y.data_ptr(), L.FP8Q_OUT_F32, 4, 4, 96, None) == L.FP8Q_ERR_SHAPE
+    assert g(p, p, None, y.data_ptr(), 7, 4, 4, 64, None) == L.FP8Q_ERR_DTYPE
+    assert g(p + 2, p, None, y.data_ptr(), L.FP8Q_OUT_F32, 4, 4, 64, None) == L.FP8Q_ERR_ALIGN
+    assert g(None, p, None, y.data_ptr(), L.FP8Q_OUT_F32, 4, 4, 64, None) == L.FP8Q_ERR_NULL
+    assert g(p, p, None, y.data_ptr(), L.FP8Q_OUT_F32, 4, 4, 1 << 23, None) == L.FP8Q_ERR_SHAPE
+    with pytest.raises(ValueError):
+        fq.bf16_gemm(X[:, :100].contiguous(), W[:, :100].contiguous())
+    assert bf16_linear_rel(7168) == (224 + 1) * 2.0 ** -24

@@ -463,29 +463,6 @@ def test_gemm_kmajor_scales_bias_and_errors():
                                    None) == L.FP8Q_ERR_DTYPE
 
 
-def test_linear_dispatch():
-    """linear(): the FP8 branch is act_quant + fp8_gemm with the bias fused; the bf16
-    branch dequantises the weight and applies torch's linear; a bf16 weight is used as is."""
-    M, N, K = 37, 300, 512
-    x = dev_bf16(synth.random_bf16((M, K), seed=41))
-    Wb = dev_bf16(synth.random_bf16((N, K), seed=42, std=0.02))
-    bias = dev_bf16(synth.random_bf16((N,), seed=43))
-    wq, sw = fq.weight_quant(Wb)
-    q, s = fq.act_quant(x)
-    ref_fp8 = fq.fp8_gemm(q, s, wq, sw, out_dtype=torch.bfloat16, bias=bias)
-    y_fp8 = fq.linear(x, wq, bias, weight_scale=sw)
-    assert torch.equal(y_fp8.view(torch.int16), ref_fp8.view(torch.int16))
-    y_bf16 = fq.linear(x, wq, bias, weight_scale=sw, gemm_impl="bf16")
-    ref_bf16 = torch.nn.functional.linear(x, fq.weight_dequant(wq, sw), bias)
-    assert torch.equal(y_bf16.view(torch.int16), ref_bf16.view(torch.int16))
-    y_pass = fq.linear(x, Wb, bias)
-    assert torch.equal(y_pass.view(torch.int16), torch.nn.functional.linear(x, Wb, bias).view(torch.int16))
-    with pytest.raises(ValueError):
-        fq.linear(x, wq, bias)   # FP8 weight without its scale
-    with pytest.raises(ValueError):
-        fq.fp8_gemm(q, s, wq, sw, bias=bias[:-1])
-
-
 @pytest.mark.parametrize("name", ["q_down", "kv_down", "kv_up", "outlier"])
 def test_gemm_workload_full_size_every_output(name):
     """Each large workload at full size, in the benchmark's launch (K-block-major activation

@@ -469,6 +469,50 @@ def test_matmul_bf16_sampled(oracle_lib):
     assert np.allclose(y, want.reshape(-1), rtol=1e-13, atol=1e-13)
 
 
+def test_matmul_bf16_small_integers_equal_integer_matmul(oracle_lib):
+    """bf16 linear (the bf16 branch of linear()): on bf16 values that are small integers times
+    a per-row and per-column power of two, every product and every partial sum is exact, so the
+    oracle must equal the integer matrix product scaled by those powers of two (numpy int64,
+    an independent routine), and its bound must equal the product of the absolute values."""
+    rng = np.random.Generator(np.random.PCG64(23))
+    M, N, K = 13, 37, 192
+    ia = rng.integers(-15, 16, size=(M, K))
+    iw = rng.integers(-15, 16, size=(N, K))
+    ea = rng.integers(-6, 7, size=(M, 1))
+    ew = rng.integers(-6, 7, size=(N, 1))
+    A = synth.bf16_bits((ia * 2.0 ** ea).astype(np.float32))
+    W = synth.bf16_bits((iw * 2.0 ** ew).astype(np.float32))
+    y, b = oracle.matmul_bf16(A, W)
+    scale = 2.0 ** (ea + ew.T)
+    assert np.array_equal(y, (ia @ iw.T) * scale)
+    assert np.array_equal(b, (np.abs(ia) @ np.abs(iw).T) * scale)
+
+
+def test_matmul_bf16_one_hot_rows(oracle_lib):
+    """A row of x with a single non-zero c at k0 gives y[m, n] = c * w[n, k0] exactly and a
+    bound of |y| (a wrong index or transposed operand picks another element of w)."""
+    M, N, K = 5, 70, 128
+    W = synth.random_bf16((N, K), 29, std=0.02)
+    A = np.zeros((M, K), dtype=np.uint16)
+    k0 = [0, 1, 63, 64, 127]
+    c = [1.0, -2.0, 0.5, 3.0, -0.25]
+    for m in range(M):
+        A[m, k0[m]] = synth.bf16_bits(np.float32([c[m]]))[0]
+    y, b = oracle.matmul_bf16(A, W)
+    w = oracle.bf16_to_f32_array(W).astype(np.float64)
+    for m in range(M):
+        assert np.array_equal(y[m], c[m] * w[:, k0[m]])
+        assert np.array_equal(b[m], np.abs(y[m]))
+
+
+def test_matmul_bf16_sampled_equals_full(oracle_lib):
+    A = synth.random_bf16((9, 320), 31)
+    W = synth.random_bf16((21, 320), 32, std=0.02)
+    y, _ = oracle.matmul_bf16(A, W)
+    r, c = np.arange(9).repeat(21), np.tile(np.arange(21), 9)
+    assert np.array_equal(oracle.matmul_bf16_sampled(A, W, r, c), y.reshape(-1))
+
+
 def test_f64_to_bf16_single_rounding(oracle_lib):
     # On doubles that are fp32 values, torch's float64 -> bfloat16 cast is one rounding and
     # must agree. Just off a bf16 midpoint (+- one float64 ulp) a correct single rounding
