@@ -11,7 +11,7 @@ import torch
 import fp8_act_quant_amd as fq
 import oracle
 import synth
-from helpers import bf16_linear_rel, check_bf16_linear_every_output, dev_bf16, host_bits16, host_codes
+from helpers import bf16_linear_rel, check_bf16_linear_every_output, dev_bf16, gemm_check, host_bits16, host_codes
 
 pytestmark = pytest.mark.gpu
 
@@ -116,3 +116,30 @@ def test_bf16_gemm_deterministic_and_error_paths():
     with pytest.raises(ValueError):
         fq.bf16_gemm(X[:, :100].contiguous(), W[:, :100].contiguous())
     assert bf16_linear_rel(7168) == (224 + 1) * 2.0 ** -24
+
+
+def test_bf16_gemm_maximum_k():
+    """The largest K the bf16 GEMM takes (2^23 - 64): a 256-row tile's byte offsets into X
+    reach 255 * 2K + 2K - 16, just below 2^32. Sampled outputs, including the tile's last row
+    and the ragged last column, against the oracle's float64 bf16 linear."""
+    M, N, K = 256, 200, (1 << 23) - 64
+    print(f"bf16 gemm maximum K {M}x{N}x{K}", flush=True)
+    g = torch.Generator(device="cuda").manual_seed(21)
+    x = torch.randn((M, K), generator=g, device="cuda", dtype=torch.bfloat16)
+    w = torch.randn((N, K), generator=g, device="cuda", dtype=torch.bfloat16) * 0.02
+    for out in ("f32", "bf16"):
+        y = fq.bf16_gemm(x, w, out_dtype=TORCH_OUT[out])
+        torch.cuda.synchronize()
+        rng = np.random.Generator(np.random.PCG64(22))
+        rows = np.concatenate([[0, 127, 128, 255, 255, 255], rng.integers(0, M, 10)]).astype(np.int64)
+        cols = np.concatenate([[0, 199, 128, 0, 127, 199], rng.integers(0, N, 10)]).astype(np.int64)
+        uniq_r, uniq_c = np.unique(rows), np.unique(cols)
+        xs = host_bits16(x[torch.from_numpy(uniq_r).cuda()])
+        ws = host_bits16(w[torch.from_numpy(uniq_c).cuda()])
+        y_hat, bound = oracle.matmul_bf16(xs, ws)
+        ri = np.searchsorted(uniq_r, rows)
+        ci = np.searchsorted(uniq_c, cols)
+        yh = (y.float().cpu().numpy() if out == "f32" else host_bits16(y))[rows, cols]
+        res = gemm_check(yh, y_hat[ri, ci], bound[ri, ci], out, rel=bf16_linear_rel(K))
+        print(f"bf16 maximum K {out}", res, flush=True)
+        assert res["violations"] == 0 and res["strict_violations"] == 0, (out, res)
