@@ -267,6 +267,26 @@ def cpu_baseline(A, W, rows: int):
     }, (aq, sa, y)
 
 
+def hbm_copy_reference(stream, nbytes: int = 1 << 30, reps: int = 20) -> dict:
+    """Attainable HBM bandwidth on this machine: a plain device-to-device copy of nbytes (read
+    nbytes, write nbytes), timed back to back with events around the loop. A second reference
+    beside the 8 TB/s datasheet peak for the HBM-bound quantiser."""
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device=stream.device)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    e0, e1 = TimingEvent(), TimingEvent()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / reps
+    del src, dst
+    return {"kernel": "torch copy_ (device to device)", "bytes_moved": 2 * nbytes, "gbs": round(2 * nbytes / t / 1e9, 1)}
+
+
 def _pct(t, q) -> float:
     import numpy as np
     return round(float(np.percentile(t, q)) * 1e6, 3)
@@ -529,6 +549,7 @@ def main() -> int:
     a1_ev.record(stream)
     torch.cuda.synchronize()
     t_aq_b2b = a0_ev.elapsed_time(a1_ev) * 1e-3 / b2b_n
+    copy_ref = hbm_copy_reference(stream)
     t_gemm = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e-3
 
     flops = 2.0 * M * N * K
@@ -586,6 +607,9 @@ def main() -> int:
             "algorithmic_bytes_per_launch": aq_bytes,
             "back_to_back_us": round(t_aq_b2b * 1e6, 3),
             "back_to_back_frac": round(aq_bytes / t_aq_b2b / 1e9 / HBM_PEAK_GBS, 4),
+            # attainable HBM rate of a plain device copy on this machine, and act_quant against it
+            "hbm_copy_reference": copy_ref,
+            "back_to_back_frac_of_copy": round(aq_bytes / t_aq_b2b / 1e9 / copy_ref["gbs"], 4),
         },
         "gemm_only_tflops": round(gemm_tflops, 2),
     }

@@ -40,6 +40,8 @@ def test_bench_json_contract():
                                            rel=1e-3)
     assert rf["traffic"] is None or rf["traffic"] > 0
     assert rf["mfma_busy_frac"] is None or 0 < rf["mfma_busy_frac"] < 1
+    aq = d["act_quant"]
+    assert aq["hbm_copy_reference"]["gbs"] > 0 and 0 < aq["back_to_back_frac_of_copy"]
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["cores"] >= 1 and cb["value"] > 0 and cb["sample"]
     assert cb["host"]["nproc"] >= 1 and cb["host"]["omp_threads"] == cb["cores"]
