@@ -94,3 +94,41 @@ def test_noalloc_refuses_plans_beyond_the_scratch():
     assert fq.lib.fp8_block_gemm_noalloc(None, None, None, None, None, L.FP8Q_OUT_BF16, 0, N, K, None) == L.FP8Q_OK
     assert fq.lib.fp8_block_gemm_noalloc(p, p, p, p, p, 3, 4, 4, 128, None) == L.FP8Q_ERR_DTYPE
     assert fq.lib.fp8_block_gemm_noalloc(p, p, p, p, p, L.FP8Q_OUT_BF16, 4, 4, 100, None) == L.FP8Q_ERR_SHAPE
+
+
+def test_noalloc_replays_in_a_captured_graph():
+    """The callers this entry point is for include code under HIP graph capture: captured once
+    (its split-K epoch is fixed at capture), the call is replayed three times with new
+    activations copied into the captured input between replays, with eager work and
+    synchronisation in between; every replay equals fp8_block_gemm with a workspace on the same
+    input, bit for bit."""
+    g = torch.Generator(device="cuda").manual_seed(79)
+    M, N, K = 4096, 576, 7168
+    code = L.FP8Q_OUT_BF16
+    assert 0 < int(fq.lib.fp8_block_gemm_workspace_bytes(M, N, K, code)) <= L.FP8Q_NOALLOC_SCRATCH_BYTES
+    wq, sw = fq.weight_quant((torch.randn((N, K), generator=g, device="cuda") * 0.02).to(torch.bfloat16))
+    aq, sa = fq.act_quant(torch.randn((M, K), generator=g, device="cuda").to(torch.bfloat16))
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    # warm up on the capture stream, then capture
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        assert _noalloc(aq, sa, wq, sw, y, code, M, N, K) == L.FP8Q_OK
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        assert _noalloc(aq, sa, wq, sw, y, code, M, N, K) == L.FP8Q_OK
+    for r in range(3):
+        aq2, sa2 = fq.act_quant(torch.randn((M, K), generator=g, device="cuda").to(torch.bfloat16))
+        aq.copy_(aq2)
+        sa.copy_(sa2)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        ref = torch.empty_like(y)
+        st, _, ws = _with_workspace(aq, sa, wq, sw, ref, code, M, N, K)
+        assert st == L.FP8Q_OK
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), ref.view(torch.int16)), (r, int((y != ref).sum()))
+        del ws
