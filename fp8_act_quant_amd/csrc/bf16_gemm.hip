@@ -12,12 +12,19 @@
 // MFMA's A operand and X rows its B operand: lane l of a 16x16 result holds n = 4*(l/16) + r
 // (r = 0..3) for m = l % 16, four consecutive outputs of a row of Y.
 //
-// Tiling. A workgroup of 8 waves owns a 256 x 128 output tile; its waves form a 4 x 2 grid
-// of 64 x 64 wave tiles (4 x 4 blocks of 16 x 16). K advances in steps of 64 elements, one
-// 128-byte piece of every tile row, copied global -> LDS by LDS-DMA loads (buffer_load ...
-// lds) into one of 3 stage buffers; 16-byte chunks of each row are XOR-swizzled by (row & 7)
-// so that the fragment reads (16 rows x 4 chunks per instruction) are free of bank
-// conflicts. Rows past M or N lie outside the loads' buffer range and read as zero.
+// Tiling. A workgroup of NW waves owns a BM x 128 output tile; its waves form a grid of 64 x 64
+// wave tiles (4 x 4 blocks of 16 x 16): 256 x 128 with 8 waves, or, for shapes with too few
+// of those tiles to fill the GPU, 128 x 128 with 4 waves (two workgroups per CU). K advances
+// in steps of 64 elements, one 128-byte piece of every tile row, copied global -> LDS by
+// LDS-DMA loads (buffer_load ... lds) into one of NSTAGE stage buffers; 16-byte chunks of
+// each row are XOR-swizzled by (row & 7) so that the fragment reads (16 rows x 4 chunks per
+// instruction) are free of bank conflicts. Rows past M or N lie outside the loads' buffer
+// range and read as zero.
+//
+// Schedule. Two register sets hold the fragments of two K steps: the MFMAs of step ks take
+// their operands from one set while the other is filled from LDS with step ks + 1, so the
+// LDS reads have a whole step of MFMA work to land behind. A stage buffer is free once its
+// step is in registers; the copies of step ks + NSTAGE go into the buffer of step ks.
 //
 // Work order. Workgroups are dealt round-robin to the 8 XCDs; the block index is remapped
 // so that each XCD walks a contiguous run of tiles, taken down `group` tile rows per tile
@@ -33,17 +40,27 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
-constexpr int BM = 256, BN = 128, NW = 8, WAVES_M = 4, WAVES_N = 2;
-constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;       // 64 x 64 per wave
-constexpr int SUB_M = WM / 16, SUB_N = WN / 16;           // 4 x 4 blocks
+constexpr int BN = 128;
 constexpr int KSTEP = 64;                                 // bf16 elements per stage row
 constexpr int ROW_BYTES = KSTEP * 2;                      // 128
-constexpr int NSTAGE = 3;
-constexpr int A_BYTES = BM * ROW_BYTES, W_BYTES = BN * ROW_BYTES;
-constexpr int STAGE = A_BYTES + W_BYTES;                  // 48 KiB
-constexpr int A_INSTR = BM / (8 * NW), W_INSTR = BN / (8 * NW);   // 1 KiB copies per wave and stage
-constexpr int IPW = A_INSTR + W_INSTR;
-static_assert(STAGE * NSTAGE <= 160 * 1024, "LDS budget");
+
+// tile configuration: BM x 128, NW waves in a WAVES_M x (NW / WAVES_M) grid, NSTAGE stages
+template <int BM_, int NW_, int WAVES_M_, int NSTAGE_>
+struct Bf16Tile {
+    static constexpr int BM = BM_, NW = NW_, WAVES_M = WAVES_M_, WAVES_N = NW_ / WAVES_M_, NSTAGE = NSTAGE_;
+    static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;      // 64 x 64 per wave
+    static constexpr int SUB_M = WM / 16, SUB_N = WN / 16;
+    static constexpr int A_BYTES = BM * ROW_BYTES, W_BYTES = BN * ROW_BYTES;
+    static constexpr int STAGE = A_BYTES + W_BYTES;
+    static constexpr int A_INSTR = BM / (8 * NW), W_INSTR = BN / (8 * NW);   // 1 KiB copies per wave and stage
+    static constexpr int IPW = A_INSTR + W_INSTR;
+    static_assert(WAVES_M * WAVES_N == NW && WM == 64 && WN == 64, "64 x 64 wave tiles");
+    static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "copy rows");
+    static_assert(STAGE * NSTAGE <= 160 * 1024, "LDS budget");
+    static_assert(NSTAGE >= 2 && IPW * (NSTAGE - 1) < 64, "stages");
+};
+using TileL = Bf16Tile<256, 8, 4, 3>;   // 256 x 128, 8 waves, 144 KiB of LDS
+using TileS = Bf16Tile<128, 4, 2, 2>;   // 128 x 128, 4 waves, 64 KiB (two workgroups per CU)
 
 struct Bf16GemmArgs {
     const uint16_t *x;
@@ -84,9 +101,109 @@ __device__ __forceinline__ f32x4 mfma_step(const u32x4 (&w)[2], const u32x4 (&x)
                                                    acc, 0, 0, 0);
 }
 
-template <int OUT_BF16>
-__global__ __launch_bounds__(NW * 64) void bf16_gemm_kernel(Bf16GemmArgs g) {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[STAGE * NSTAGE];
+// This wave's LDS-DMA copies. Instruction t of wave w moves tile rows 8 (NW t + w) .. + 7
+// of X (t < A_INSTR), then of W; lane L fills LDS row L / 8 of those 8, physical chunk L % 8,
+// i.e. loads the logical chunk that swz_chunk maps there. OUT_BF16 makes the type unique to
+// each kernel instantiation (the host pass emits a launch stub for only one kernel among
+// those that share such a type, and the resource type may appear in no signature it sees).
+template <class T, int OUT_BF16>
+struct Bf16Dma {
+    rsrc_t rx, rw;
+    uint32_t off[T::IPW];
+    int wave;
+    uint8_t *smem;
+
+    __device__ __forceinline__ Bf16Dma(const uint16_t *x, const uint16_t *w, int64_t m0, int64_t n0, int64_t M,
+                                       int64_t N, int64_t K, int wave_, int lane, uint8_t *smem_)
+        : wave(wave_), smem(smem_) {
+        const int64_t row_bytes = K * 2;
+        rx = make_rsrc(x + m0 * K, (M - m0 < T::BM ? M - m0 : T::BM) * row_bytes);
+        rw = make_rsrc(w + n0 * K, (N - n0 < BN ? N - n0 : BN) * row_bytes);
+        const int sub = lane >> 3;
+#pragma unroll
+        for (int t = 0; t < T::IPW; ++t) {
+            const int tt = t < T::A_INSTR ? t : t - T::A_INSTR;
+            const int row = 8 * (T::NW * tt + wave) + sub;
+            off[t] = (uint32_t)(row * row_bytes) + (swz_chunk(row, lane & 7) << 4);
+        }
+    }
+
+    // the copies of K step ks into its stage buffer
+    __device__ __forceinline__ void issue(int ks) const {
+        uint8_t *base = smem + (ks % T::NSTAGE) * T::STAGE;
+        const int koff = __builtin_amdgcn_readfirstlane(ks * ROW_BYTES);
+#pragma unroll
+        for (int t = 0; t < T::IPW; ++t) {
+            if (t < T::A_INSTR)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void *)(base + 8 * (T::NW * t + wave) * ROW_BYTES),
+                                                         16, off[t], koff, 0, 0);
+            else
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rw, (lds_void *)(base + T::A_BYTES + 8 * (T::NW * (t - T::A_INSTR) + wave) * ROW_BYTES), 16,
+                    off[t], koff, 0, 0);
+        }
+    }
+};
+
+// this wave's fragments of K step ks: W column groups, then X row groups
+template <class T>
+__device__ __forceinline__ void read_step(const uint8_t *smem, int ks, int a_base, int w_base, int lo, int hi,
+                                          u32x4 (&wf)[T::SUB_N][2], u32x4 (&xf)[T::SUB_M][2]) {
+    const uint8_t *stage = smem + (ks % T::NSTAGE) * T::STAGE;
+#pragma unroll
+    for (int j = 0; j < T::SUB_N; ++j) {
+        wf[j][0] = *reinterpret_cast<const u32x4 *>(stage + w_base + 16 * j * ROW_BYTES + lo);
+        wf[j][1] = *reinterpret_cast<const u32x4 *>(stage + w_base + 16 * j * ROW_BYTES + hi);
+    }
+#pragma unroll
+    for (int i = 0; i < T::SUB_M; ++i) {
+        xf[i][0] = *reinterpret_cast<const u32x4 *>(stage + a_base + 16 * i * ROW_BYTES + lo);
+        xf[i][1] = *reinterpret_cast<const u32x4 *>(stage + a_base + 16 * i * ROW_BYTES + hi);
+    }
+}
+
+template <class T>
+__device__ __forceinline__ void wait_step_landed(int queued_after) {
+    // loads retire in issue order: a step has landed once at most the copies of the
+    // `queued_after` steps issued after it are in flight
+    if constexpr (T::NSTAGE >= 3) {
+        if (queued_after >= 1) {
+            wait_vmcnt<T::IPW * (T::NSTAGE - 2)>();
+            return;
+        }
+    }
+    wait_vmcnt<0>();
+}
+
+// K step ks, whose fragments are in (wf, xf): once every wave has them in registers (the
+// barrier) its stage buffer takes step ks + NSTAGE; step ks + 1, visible after the same
+// barrier, is read into (wf_next, xf_next) while the MFMAs of step ks run
+template <class T, class Dma>
+__device__ __forceinline__ void k_step(int ks, int nks, const Dma &dma, const uint8_t *smem, int a_base, int w_base,
+                                       int lo, int hi,
+                                       const u32x4 (&wf)[T::SUB_N][2], const u32x4 (&xf)[T::SUB_M][2],
+                                       u32x4 (&wf_next)[T::SUB_N][2], u32x4 (&xf_next)[T::SUB_M][2],
+                                       f32x4 (&acc)[T::SUB_M][T::SUB_N]) {
+    const bool more = ks + 1 < nks;
+    __builtin_amdgcn_sched_barrier(0);   // the waits stay behind the previous step's MFMAs
+    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));   // lgkmcnt(0): (wf, xf) have landed
+    if (more) wait_step_landed<T>(min(nks - 2 - ks, T::NSTAGE - 2));
+    lds_barrier();
+    if (ks + T::NSTAGE < nks) dma.issue(ks + T::NSTAGE);
+    if (more) read_step<T>(smem, ks + 1, a_base, w_base, lo, hi, wf_next, xf_next);
+#pragma unroll
+    for (int i = 0; i < T::SUB_M; ++i)
+#pragma unroll
+        for (int j = 0; j < T::SUB_N; ++j) acc[i][j] = mfma_step(wf[j], xf[i], acc[i][j]);
+}
+
+template <int BM_, int NW_, int WAVES_M_, int NSTAGE_, int OUT_BF16>
+__global__ __launch_bounds__(NW_ * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void bf16_gemm_kernel(
+    Bf16GemmArgs g) {   // (2 waves per SIMD: the 4-wave tile runs two workgroups per CU)
+    using T = Bf16Tile<BM_, NW_, WAVES_M_, NSTAGE_>;
+    constexpr int NW = T::NW, WAVES_M = T::WAVES_M, WM = T::WM, WN = T::WN, SUB_M = T::SUB_M, SUB_N = T::SUB_N;
+    constexpr int BM = T::BM, NSTAGE = T::NSTAGE, IPW = T::IPW;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[T::STAGE * NSTAGE];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -104,35 +221,8 @@ __global__ __launch_bounds__(NW * 64) void bf16_gemm_kernel(Bf16GemmArgs g) {
     const int64_t m0 = (int64_t)(band * g.group + in_band % band_rows) * BM;
     const int64_t n0 = (int64_t)(in_band / band_rows) * BN;
     const int64_t M = g.M, N = g.N, K = g.K;
-    const int64_t row_bytes = K * 2;
     const int nks = (int)(K / KSTEP);
-
-    // copies: instruction t of wave w moves tile rows 8 (NW t + w) .. + 7; lane L fills
-    // LDS row L / 8, physical chunk L % 8, i.e. loads the logical chunk swz_chunk maps there
-    const rsrc_t rx = make_rsrc(g.x + m0 * K, (M - m0 < BM ? M - m0 : BM) * row_bytes);
-    const rsrc_t rw = make_rsrc(g.w + n0 * K, (N - n0 < BN ? N - n0 : BN) * row_bytes);
-    uint32_t off[IPW];
-    const int sub = lane >> 3;
-#pragma unroll
-    for (int t = 0; t < IPW; ++t) {
-        const int tt = t < A_INSTR ? t : t - A_INSTR;
-        const int row = 8 * (NW * tt + wave) + sub;
-        off[t] = (uint32_t)(row * row_bytes) + (swz_chunk(row, lane & 7) << 4);
-    }
-    auto issue = [&](int ks, int st) __device__ __attribute__((always_inline)) {
-        const int koff = __builtin_amdgcn_readfirstlane(ks * ROW_BYTES);
-        uint8_t *base = smem + st * STAGE;
-#pragma unroll
-        for (int t = 0; t < IPW; ++t) {
-            if (t < A_INSTR)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void *)(base + 8 * (NW * t + wave) * ROW_BYTES), 16,
-                                                         off[t], koff, 0, 0);
-            else
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rw, (lds_void *)(base + A_BYTES + 8 * (NW * (t - A_INSTR) + wave) * ROW_BYTES), 16, off[t], koff,
-                    0, 0);
-        }
-    };
+    const Bf16Dma<T, OUT_BF16> dma(g.x, g.w, m0, n0, M, N, K, wave, lane, smem);
 
     f32x4 acc[SUB_M][SUB_N];
 #pragma unroll
@@ -145,40 +235,22 @@ __global__ __launch_bounds__(NW * 64) void bf16_gemm_kernel(Bf16GemmArgs g) {
     const int frow = lane & 15, kg = lane >> 4;
     const int lo = frow * ROW_BYTES + (swz_chunk(frow, kg) << 4);
     const int hi = frow * ROW_BYTES + (swz_chunk(frow, 4 + kg) << 4);
-    const int a_base = wm * WM * ROW_BYTES, w_base = A_BYTES + wn * WN * ROW_BYTES;
-    auto frag = [&](const uint8_t *p, u32x4 (&f)[2]) __device__ __attribute__((always_inline)) {
-        f[0] = *reinterpret_cast<const u32x4 *>(p + lo);
-        f[1] = *reinterpret_cast<const u32x4 *>(p + hi);
-    };
+    const int a_base = wm * WM * ROW_BYTES, w_base = T::A_BYTES + wn * WN * ROW_BYTES;
 
-    // prologue: the first NSTAGE - 1 steps in flight
+    if (nks > 0) {
+        // two register sets of fragments; step ks uses set ks % 2
+        u32x4 wf0[SUB_N][2], xf0[SUB_M][2], wf1[SUB_N][2], xf1[SUB_M][2];
+        // prologue: the first NSTAGE steps in flight, step 0 read into set 0
 #pragma unroll
-    for (int s = 0; s < NSTAGE - 1; ++s)
-        if (s < nks) issue(s, s);
-
-    for (int ks = 0; ks < nks; ++ks) {
-        const int st = ks % NSTAGE;
-        // step ks has landed once at most the copies of the steps queued after it are in
-        // flight (loads retire in issue order); then every wave's copies are visible after
-        // the barrier, which also means every wave is done reading step ks - 1
-        if (ks + 1 < nks) wait_vmcnt<IPW * (NSTAGE - 2)>();
+        for (int s = 0; s < NSTAGE; ++s)
+            if (s < nks) dma.issue(s);
+        if (nks >= NSTAGE) wait_vmcnt<IPW * (NSTAGE - 1)>();
         else wait_vmcnt<0>();
         lds_barrier();
-        if (ks + NSTAGE - 1 < nks) issue(ks + NSTAGE - 1, (ks + NSTAGE - 1) % NSTAGE);
-        const uint8_t *stage = smem + st * STAGE;
-        u32x4 wf[SUB_N][2], xf[2], xn[2];
-#pragma unroll
-        for (int j = 0; j < SUB_N; ++j) frag(stage + w_base + 16 * j * ROW_BYTES, wf[j]);
-        frag(stage + a_base, xf);
-#pragma unroll
-        for (int i = 0; i < SUB_M; ++i) {
-            if (i + 1 < SUB_M) frag(stage + a_base + 16 * (i + 1) * ROW_BYTES, xn);
-#pragma unroll
-            for (int j = 0; j < SUB_N; ++j) acc[i][j] = mfma_step(wf[j], xf, acc[i][j]);
-            if (i + 1 < SUB_M) {
-                xf[0] = xn[0];
-                xf[1] = xn[1];
-            }
+        read_step<T>(smem, 0, a_base, w_base, lo, hi, wf0, xf0);
+        for (int ks = 0; ks < nks; ks += 2) {
+            k_step<T>(ks, nks, dma, smem, a_base, w_base, lo, hi, wf0, xf0, wf1, xf1, acc);
+            if (ks + 1 < nks) k_step<T>(ks + 1, nks, dma, smem, a_base, w_base, lo, hi, wf1, xf1, wf0, xf0, acc);
         }
     }
 
@@ -222,31 +294,45 @@ __global__ __launch_bounds__(NW * 64) void bf16_gemm_kernel(Bf16GemmArgs g) {
 
 }  // namespace
 
-hipError_t launch_bf16_gemm(const uint16_t *x, const uint16_t *w, const float *bias, void *y, bool out_bf16, int64_t M,
-                            int64_t N, int64_t K, hipStream_t stream) {
-    if (M == 0 || N == 0) return hipSuccess;
-    Bf16GemmArgs a{x, w, bias, y, M, N, K, (int)((M + BM - 1) / BM), (int)((N + BN - 1) / BN), 1};
+namespace {
+
+template <class T>
+hipError_t launch_tile(Bf16GemmArgs a, bool out_bf16, hipStream_t stream) {
+    a.tiles_m = (int)((a.M + T::BM - 1) / T::BM);
+    a.tiles_n = (int)((a.N + BN - 1) / BN);
     // group: tile rows walked per tile column, so that an XCD's ~32 resident tiles form a
-    // compact block (fewest A + W rows); as in the block GEMM's planner
+    // compact block (fewest A + W rows)
     int64_t best_rows = -1;
     for (int gsz = 1; gsz <= 32; gsz *= 2) {
         const int64_t gg = gsz < a.tiles_m ? gsz : a.tiles_m;
         const int64_t cols = (32 + gg - 1) / gg;
-        const int64_t rows = gg * BM + (cols < a.tiles_n ? cols : a.tiles_n) * BN;
+        const int64_t rows = gg * T::BM + (cols < a.tiles_n ? cols : a.tiles_n) * BN;
         if (best_rows < 0 || rows < best_rows) {
             best_rows = rows;
             a.group = gsz;
         }
     }
     const int64_t tiles = (int64_t)a.tiles_m * a.tiles_n;
-    if (tiles * NW * 64 > 0xFFFFFFFFll) return hipErrorInvalidValue;
-    const dim3 grid((unsigned)tiles), block(NW * 64);
+    if (tiles * T::NW * 64 > 0xFFFFFFFFll) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)tiles), block(T::NW * 64);
     // (K = 0 runs no K step: Y is the bias, or zero)
     if (out_bf16)
-        bf16_gemm_kernel<1><<<grid, block, 0, stream>>>(a);
+        bf16_gemm_kernel<T::BM, T::NW, T::WAVES_M, T::NSTAGE, 1><<<grid, block, 0, stream>>>(a);
     else
-        bf16_gemm_kernel<0><<<grid, block, 0, stream>>>(a);
+        bf16_gemm_kernel<T::BM, T::NW, T::WAVES_M, T::NSTAGE, 0><<<grid, block, 0, stream>>>(a);
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bf16_gemm(const uint16_t *x, const uint16_t *w, const float *bias, void *y, bool out_bf16, int64_t M,
+                            int64_t N, int64_t K, hipStream_t stream) {
+    if (M == 0 || N == 0) return hipSuccess;
+    Bf16GemmArgs a{x, w, bias, y, M, N, K, 0, 0, 1};
+    // the 256-row tile where its tiles fill the 256 CUs, else the 128-row one (two per CU)
+    const int64_t large_tiles = ((M + TileL::BM - 1) / TileL::BM) * ((N + BN - 1) / BN);
+    if (large_tiles >= 256) return launch_tile<TileL>(a, out_bf16, stream);
+    return launch_tile<TileS>(a, out_bf16, stream);
 }
 
 }  // namespace fp8q
