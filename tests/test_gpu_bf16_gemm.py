@@ -21,7 +21,7 @@ TORCH_OUT = {"f32": torch.float32, "bf16": torch.bfloat16}
 @pytest.mark.parametrize("with_bias", [False, True])
 @pytest.mark.parametrize("out", ["f32", "bf16"])
 @pytest.mark.parametrize("M,N,K", [(1, 1, 64), (37, 200, 384), (300, 576, 256), (256, 128, 64), (513, 129, 1024),
-                                   (260, 1000, 1536)])
+                                   (260, 1000, 1536), (130, 260, 448)])
 def test_bf16_gemm_small_every_output(M, N, K, out, with_bias):
     X = synth.random_bf16((M, K), seed=M + 3 * N + K)
     W = synth.random_bf16((N, K), seed=5 * M + N + K, std=0.02)
@@ -33,6 +33,23 @@ def test_bf16_gemm_small_every_output(M, N, K, out, with_bias):
     assert res["n"] == M * N
     # (with a bias, the one fp32 rounding of the addition is part of the bound: violations)
     assert res["violations"] == 0 and (with_bias or res["strict_violations"] == 0), res
+
+
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+@pytest.mark.parametrize("K", [64, 320, 512])
+def test_bf16_gemm_large_tile_every_output(K, out):
+    """A shape with at least 256 tiles of 256x128 (17 x 17 here, ragged in both M and N),
+    which takes the 8-wave 256x128 tile rather than the 128x128 one; K of 1, 5 and 8 steps
+    of 64 (an odd step count ends on the first register set)."""
+    M, N = 4100, 2050
+    X = synth.random_bf16((M, K), seed=K + 11)
+    W = synth.random_bf16((N, K), seed=K + 12, std=0.02)
+    print(f"bf16 gemm large tile {M}x{N}x{K} {out}", flush=True)
+    y = fq.bf16_gemm(dev_bf16(X), dev_bf16(W), out_dtype=TORCH_OUT[out])
+    torch.cuda.synchronize()
+    res = check_bf16_linear_every_output(y, X, W, out, f"bf16 gemm {M}x{N}x{K} {out}")
+    assert res["n"] == M * N
+    assert res["violations"] == 0 and res["strict_violations"] == 0, res
 
 
 def test_bf16_gemm_k_zero_is_bias_and_empty_m():
