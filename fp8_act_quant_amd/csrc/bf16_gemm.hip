@@ -12,23 +12,30 @@
 // MFMA's A operand and X rows its B operand: lane l of a 16x16 result holds n = 4*(l/16) + r
 // (r = 0..3) for m = l % 16, four consecutive outputs of a row of Y.
 //
-// Tiling. A workgroup of NW waves owns a BM x 128 output tile; its waves form a grid of 64 x 64
-// wave tiles (4 x 4 blocks of 16 x 16): 256 x 128 with 8 waves, or, for shapes with too few
-// of those tiles to fill the GPU, 128 x 128 with 4 waves (two workgroups per CU). K advances
-// in steps of 64 elements, one 128-byte piece of every tile row, copied global -> LDS by
-// LDS-DMA loads (buffer_load ... lds) into one of NSTAGE stage buffers; 16-byte chunks of
-// each row are XOR-swizzled by (row & 7) so that the fragment reads (16 rows x 4 chunks per
-// instruction) are free of bank conflicts. Rows past M or N lie outside the loads' buffer
-// range and read as zero.
+// Tiling. Two tiles: 256 x 256 with 8 waves of 128 x 64 (8 x 4 blocks of 16 x 16) where
+// such tiles fill the 256 CUs, else 128 x 128 with 4 waves of 64 x 64 (two workgroups per
+// CU). K advances in steps of 64 elements, one 128-byte piece of every tile row, copied
+// global -> LDS by LDS-DMA loads (buffer_load ... lds) into one of NSTAGE stage buffers;
+// 16-byte chunks of each row are XOR-swizzled by (row & 7) so that the fragment reads (16
+// rows x 4 chunks per instruction) are free of bank conflicts. Rows past M or N lie outside
+// the loads' buffer range and read as zero.
 //
-// Schedule. Two register sets hold the fragments of two K steps: the MFMAs of step ks take
-// their operands from one set while the other is filled from LDS with step ks + 1, so the
-// LDS reads have a whole step of MFMA work to land behind. A stage buffer is free once its
-// step is in registers; the copies of step ks + NSTAGE go into the buffer of step ks.
+// Schedule. 64 x 64 wave tiles: two register sets hold the fragments of two K steps; the
+// MFMAs of step ks take their operands from one set while the other is filled from LDS with
+// step ks + 1, so the LDS reads have a whole step of MFMA work to land behind, and a stage
+// buffer is free once its step is in registers (the copies of step ks + NSTAGE go into the
+// buffer of step ks). 128 x 64 wave tiles (two such sets do not fit beside 128 accumulator
+// registers): the step's W fragments are read first and its A fragments one row group
+// ahead of their MFMAs. Per step a 128 x 64 wave reads 24 KB of fragments for 1024 cycles
+// of MFMA work, a 64 x 64 one 16 KB for 512, which is why the larger tile leads where it
+// fills the GPU.
 //
 // Work order. Workgroups are dealt round-robin to the 8 XCDs; the block index is remapped
 // so that each XCD walks a contiguous run of tiles, taken down `group` tile rows per tile
 // column, so that the tiles one XCD holds at once share A and W panels in its L2.
+#include <cstdlib>
+#include <cstring>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -40,27 +47,30 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
-constexpr int BN = 128;
 constexpr int KSTEP = 64;                                 // bf16 elements per stage row
 constexpr int ROW_BYTES = KSTEP * 2;                      // 128
 
-// tile configuration: BM x 128, NW waves in a WAVES_M x (NW / WAVES_M) grid, NSTAGE stages
-template <int BM_, int NW_, int WAVES_M_, int NSTAGE_>
+// tile configuration: BM x BN, NW waves in a WAVES_M x (NW / WAVES_M) grid, NSTAGE stages
+template <int BM_, int BN_, int NW_, int WAVES_M_, int NSTAGE_>
 struct Bf16Tile {
-    static constexpr int BM = BM_, NW = NW_, WAVES_M = WAVES_M_, WAVES_N = NW_ / WAVES_M_, NSTAGE = NSTAGE_;
-    static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;      // 64 x 64 per wave
+    static constexpr int BM = BM_, BN = BN_, NW = NW_, WAVES_M = WAVES_M_, WAVES_N = NW_ / WAVES_M_;
+    static constexpr int NSTAGE = NSTAGE_;
+    static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;      // wave tile
     static constexpr int SUB_M = WM / 16, SUB_N = WN / 16;
     static constexpr int A_BYTES = BM * ROW_BYTES, W_BYTES = BN * ROW_BYTES;
     static constexpr int STAGE = A_BYTES + W_BYTES;
     static constexpr int A_INSTR = BM / (8 * NW), W_INSTR = BN / (8 * NW);   // 1 KiB copies per wave and stage
     static constexpr int IPW = A_INSTR + W_INSTR;
-    static_assert(WAVES_M * WAVES_N == NW && WM == 64 && WN == 64, "64 x 64 wave tiles");
+    // register prefetch of whole steps where two sets of a step's fragments fit (64 x 64 wave
+    // tiles); the 128 x 64 wave tile streams its A fragments through the step instead
+    static constexpr bool PF = WM == 64;
+    static_assert(WAVES_M * WAVES_N == NW && WN == 64 && (WM == 64 || WM == 128), "wave tiles");
     static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "copy rows");
     static_assert(STAGE * NSTAGE <= 160 * 1024, "LDS budget");
     static_assert(NSTAGE >= 2 && IPW * (NSTAGE - 1) < 64, "stages");
 };
-using TileL = Bf16Tile<256, 8, 4, 3>;   // 256 x 128, 8 waves, 144 KiB of LDS
-using TileS = Bf16Tile<128, 4, 2, 2>;   // 128 x 128, 4 waves, 64 KiB (two workgroups per CU)
+using TileXL = Bf16Tile<256, 256, 8, 2, 2>;   // 256 x 256, 8 waves of 128 x 64, 128 KiB of LDS
+using TileS = Bf16Tile<128, 128, 4, 2, 2>;    // 128 x 128, 4 waves, 64 KiB (two workgroups per CU)
 
 struct Bf16GemmArgs {
     const uint16_t *x;
@@ -118,7 +128,7 @@ struct Bf16Dma {
         : wave(wave_), smem(smem_) {
         const int64_t row_bytes = K * 2;
         rx = make_rsrc(x + m0 * K, (M - m0 < T::BM ? M - m0 : T::BM) * row_bytes);
-        rw = make_rsrc(w + n0 * K, (N - n0 < BN ? N - n0 : BN) * row_bytes);
+        rw = make_rsrc(w + n0 * K, (N - n0 < T::BN ? N - n0 : T::BN) * row_bytes);
         const int sub = lane >> 3;
 #pragma unroll
         for (int t = 0; t < T::IPW; ++t) {
@@ -197,12 +207,56 @@ __device__ __forceinline__ void k_step(int ks, int nks, const Dma &dma, const ui
         for (int j = 0; j < T::SUB_N; ++j) acc[i][j] = mfma_step(wf[j], xf[i], acc[i][j]);
 }
 
-template <int BM_, int NW_, int WAVES_M_, int NSTAGE_, int OUT_BF16>
+// All K steps with the A fragments streamed (the 128 x 64 wave tile, two stages). Per step:
+// the W fragments are read first, then row group by row group the next group's A fragment is
+// read while the current group's MFMAs run; at the end of the step every wave has read the
+// step (the lgkmcnt wait) and waited for the next step's copies, and after the barrier the
+// freed buffer takes the copies of step ks + 2, one step of lead.
+template <class T, class Dma>
+__device__ __forceinline__ void stream_steps(int nks, const Dma &dma, const uint8_t *smem, int a_base, int w_base,
+                                             int lo, int hi, f32x4 (&acc)[T::SUB_M][T::SUB_N]) {
+    static_assert(T::NSTAGE == 2, "two stages");
+    dma.issue(0);
+    if (nks > 1) dma.issue(1);
+    if (nks > 1) wait_vmcnt<T::IPW>();
+    else wait_vmcnt<0>();
+    lds_barrier();
+    for (int ks = 0; ks < nks; ++ks) {
+        const uint8_t *stage = smem + (ks & 1) * T::STAGE;
+        u32x4 wf[T::SUB_N][2];
+#pragma unroll
+        for (int j = 0; j < T::SUB_N; ++j) {
+            wf[j][0] = *reinterpret_cast<const u32x4 *>(stage + w_base + 16 * j * ROW_BYTES + lo);
+            wf[j][1] = *reinterpret_cast<const u32x4 *>(stage + w_base + 16 * j * ROW_BYTES + hi);
+        }
+        u32x4 xa[2] = {*reinterpret_cast<const u32x4 *>(stage + a_base + lo),
+                       *reinterpret_cast<const u32x4 *>(stage + a_base + hi)};
+#pragma unroll
+        for (int i = 0; i < T::SUB_M; ++i) {
+            u32x4 xn[2] = {xa[0], xa[1]};
+            if (i + 1 < T::SUB_M) {
+                xn[0] = *reinterpret_cast<const u32x4 *>(stage + a_base + 16 * (i + 1) * ROW_BYTES + lo);
+                xn[1] = *reinterpret_cast<const u32x4 *>(stage + a_base + 16 * (i + 1) * ROW_BYTES + hi);
+            }
+#pragma unroll
+            for (int j = 0; j < T::SUB_N; ++j) acc[i][j] = mfma_step(wf[j], xa, acc[i][j]);
+            xa[0] = xn[0];
+            xa[1] = xn[1];
+        }
+        __builtin_amdgcn_sched_barrier(0);   // the waits stay behind this step's MFMAs
+        __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));   // lgkmcnt(0)
+        if (ks + 1 < nks) wait_vmcnt<0>();   // step ks + 1 has landed
+        lds_barrier();
+        if (ks + 2 < nks) dma.issue(ks + 2);
+    }
+}
+
+template <int BM_, int BN_, int NW_, int WAVES_M_, int NSTAGE_, int OUT_BF16>
 __global__ __launch_bounds__(NW_ * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void bf16_gemm_kernel(
     Bf16GemmArgs g) {   // (2 waves per SIMD: the 4-wave tile runs two workgroups per CU)
-    using T = Bf16Tile<BM_, NW_, WAVES_M_, NSTAGE_>;
+    using T = Bf16Tile<BM_, BN_, NW_, WAVES_M_, NSTAGE_>;
     constexpr int NW = T::NW, WAVES_M = T::WAVES_M, WM = T::WM, WN = T::WN, SUB_M = T::SUB_M, SUB_N = T::SUB_N;
-    constexpr int BM = T::BM, NSTAGE = T::NSTAGE, IPW = T::IPW;
+    constexpr int BM = T::BM, BN = T::BN, NSTAGE = T::NSTAGE, IPW = T::IPW;
     __shared__ __attribute__((aligned(16))) uint8_t smem[T::STAGE * NSTAGE];
 
     const int lane = threadIdx.x & 63;
@@ -237,7 +291,9 @@ __global__ __launch_bounds__(NW_ * 64) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int hi = frow * ROW_BYTES + (swz_chunk(frow, 4 + kg) << 4);
     const int a_base = wm * WM * ROW_BYTES, w_base = T::A_BYTES + wn * WN * ROW_BYTES;
 
-    if (nks > 0) {
+    if constexpr (!T::PF) {
+        if (nks > 0) stream_steps<T>(nks, dma, smem, a_base, w_base, lo, hi, acc);
+    } else if (nks > 0) {
         // two register sets of fragments; step ks uses set ks % 2
         u32x4 wf0[SUB_N][2], xf0[SUB_M][2], wf1[SUB_N][2], xf1[SUB_M][2];
         // prologue: the first NSTAGE steps in flight, step 0 read into set 0
@@ -299,14 +355,14 @@ namespace {
 template <class T>
 hipError_t launch_tile(Bf16GemmArgs a, bool out_bf16, hipStream_t stream) {
     a.tiles_m = (int)((a.M + T::BM - 1) / T::BM);
-    a.tiles_n = (int)((a.N + BN - 1) / BN);
+    a.tiles_n = (int)((a.N + T::BN - 1) / T::BN);
     // group: tile rows walked per tile column, so that an XCD's ~32 resident tiles form a
     // compact block (fewest A + W rows)
     int64_t best_rows = -1;
     for (int gsz = 1; gsz <= 32; gsz *= 2) {
         const int64_t gg = gsz < a.tiles_m ? gsz : a.tiles_m;
         const int64_t cols = (32 + gg - 1) / gg;
-        const int64_t rows = gg * T::BM + (cols < a.tiles_n ? cols : a.tiles_n) * BN;
+        const int64_t rows = gg * T::BM + (cols < a.tiles_n ? cols : a.tiles_n) * T::BN;
         if (best_rows < 0 || rows < best_rows) {
             best_rows = rows;
             a.group = gsz;
@@ -317,9 +373,9 @@ hipError_t launch_tile(Bf16GemmArgs a, bool out_bf16, hipStream_t stream) {
     const dim3 grid((unsigned)tiles), block(T::NW * 64);
     // (K = 0 runs no K step: Y is the bias, or zero)
     if (out_bf16)
-        bf16_gemm_kernel<T::BM, T::NW, T::WAVES_M, T::NSTAGE, 1><<<grid, block, 0, stream>>>(a);
+        bf16_gemm_kernel<T::BM, T::BN, T::NW, T::WAVES_M, T::NSTAGE, 1><<<grid, block, 0, stream>>>(a);
     else
-        bf16_gemm_kernel<T::BM, T::NW, T::WAVES_M, T::NSTAGE, 0><<<grid, block, 0, stream>>>(a);
+        bf16_gemm_kernel<T::BM, T::BN, T::NW, T::WAVES_M, T::NSTAGE, 0><<<grid, block, 0, stream>>>(a);
     return hipGetLastError();
 }
 
@@ -329,9 +385,14 @@ hipError_t launch_bf16_gemm(const uint16_t *x, const uint16_t *w, const float *b
                             int64_t N, int64_t K, hipStream_t stream) {
     if (M == 0 || N == 0) return hipSuccess;
     Bf16GemmArgs a{x, w, bias, y, M, N, K, 0, 0, 1};
-    // the 256-row tile where its tiles fill the 256 CUs, else the 128-row one (two per CU)
-    const int64_t large_tiles = ((M + TileL::BM - 1) / TileL::BM) * ((N + BN - 1) / BN);
-    if (large_tiles >= 256) return launch_tile<TileL>(a, out_bf16, stream);
+    // the 256 x 256 tile where its tiles fill the 256 CUs, else the 128 x 128 one (two
+    // workgroups per CU); FP8Q_BF16_TILE=256x256 or 128x128 forces one (tuning and tests)
+    if (const char *e = std::getenv("FP8Q_BF16_TILE")) {
+        if (std::strcmp(e, "256x256") == 0) return launch_tile<TileXL>(a, out_bf16, stream);
+        if (std::strcmp(e, "128x128") == 0) return launch_tile<TileS>(a, out_bf16, stream);
+    }
+    const int64_t xl_tiles = ((M + TileXL::BM - 1) / TileXL::BM) * ((N + TileXL::BN - 1) / TileXL::BN);
+    if (xl_tiles >= 256) return launch_tile<TileXL>(a, out_bf16, stream);
     return launch_tile<TileS>(a, out_bf16, stream);
 }
 

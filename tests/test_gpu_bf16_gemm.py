@@ -38,10 +38,10 @@ def test_bf16_gemm_small_every_output(M, N, K, out, with_bias):
 @pytest.mark.parametrize("out", ["f32", "bf16"])
 @pytest.mark.parametrize("K", [64, 320, 512])
 def test_bf16_gemm_large_tile_every_output(K, out):
-    """A shape with at least 256 tiles of 256x128 (17 x 17 here, ragged in both M and N),
-    which takes the 8-wave 256x128 tile rather than the 128x128 one; K of 1, 5 and 8 steps
-    of 64 (an odd step count ends on the first register set)."""
-    M, N = 4100, 2050
+    """A shape with at least 256 tiles of 256x256 (17 x 17 here, ragged in both M and N),
+    which takes the 8-wave 256x256 tile (A fragments streamed through each K step) rather
+    than the 128x128 one; K of 1, 5 and 8 steps of 64."""
+    M, N = 4100, 4097
     X = synth.random_bf16((M, K), seed=K + 11)
     W = synth.random_bf16((N, K), seed=K + 12, std=0.02)
     print(f"bf16 gemm large tile {M}x{N}x{K} {out}", flush=True)
@@ -50,6 +50,23 @@ def test_bf16_gemm_large_tile_every_output(K, out):
     res = check_bf16_linear_every_output(y, X, W, out, f"bf16 gemm {M}x{N}x{K} {out}")
     assert res["n"] == M * N
     assert res["violations"] == 0 and res["strict_violations"] == 0, res
+
+
+@pytest.mark.parametrize("tile", ["256x256", "128x128"])
+@pytest.mark.parametrize("M,N,K", [(1, 1, 64), (300, 260, 448), (513, 129, 1024), (257, 511, 128)])
+def test_bf16_gemm_each_tile_every_output(tile, M, N, K, monkeypatch):
+    """Each tile forced (FP8Q_BF16_TILE) on small ragged shapes, both output dtypes, with a
+    bias: partial tiles in M and N, odd and even step counts."""
+    monkeypatch.setenv("FP8Q_BF16_TILE", tile)
+    X = synth.random_bf16((M, K), seed=7 * M + N + K)
+    W = synth.random_bf16((N, K), seed=M + 5 * N + K, std=0.02)
+    bias = np.random.Generator(np.random.PCG64(N + 9)).standard_normal(N).astype(np.float32)
+    for out in ("f32", "bf16"):
+        y = fq.bf16_gemm(dev_bf16(X), dev_bf16(W), torch.from_numpy(bias).cuda(), out_dtype=TORCH_OUT[out])
+        torch.cuda.synchronize()
+        res = check_bf16_linear_every_output(y, X, W, out, f"bf16 gemm {tile} {M}x{N}x{K} {out}", bias)
+        assert res["n"] == M * N
+        assert res["violations"] == 0, res
 
 
 def test_bf16_gemm_k_zero_is_bias_and_empty_m():
@@ -135,10 +152,12 @@ def test_bf16_gemm_deterministic_and_error_paths():
     assert bf16_linear_rel(7168) == (224 + 1) * 2.0 ** -24
 
 
-def test_bf16_gemm_maximum_k():
-    """The largest K the bf16 GEMM takes (2^23 - 64): a 256-row tile's byte offsets into X
-    reach 255 * 2K + 2K - 16, just below 2^32. Sampled outputs, including the tile's last row
-    and the ragged last column, against the oracle's float64 bf16 linear."""
+def test_bf16_gemm_maximum_k(monkeypatch):
+    """The largest K the bf16 GEMM takes (2^23 - 64), on the 256x256 tile (forced): a
+    256-row tile's byte offsets into X reach 255 * 2K + 2K - 16, just below 2^32. Sampled
+    outputs, including the tile's last row and the ragged last column, against the oracle's
+    float64 bf16 linear."""
+    monkeypatch.setenv("FP8Q_BF16_TILE", "256x256")
     M, N, K = 256, 200, (1 << 23) - 64
     print(f"bf16 gemm maximum K {M}x{N}x{K}", flush=True)
     g = torch.Generator(device="cuda").manual_seed(21)
