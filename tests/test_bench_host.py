@@ -112,7 +112,7 @@ def test_counter_files_are_per_workload():
 
 def test_cpu_sample_is_bounded():
     """The CPU baseline's row sample is about 1e11 multiply-adds (a few seconds of the oracle on
-    a GPU machine's host share), a multiple of 64 rows, never more than the workload's rows."""
+    16 host cores), a multiple of 64 rows, never more than the workload's rows."""
     import synth
     for wl in synth.WORKLOADS.values():
         r = bench.cpu_sample_rows(wl.M, wl.N, wl.K)
