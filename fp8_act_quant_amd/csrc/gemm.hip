@@ -771,6 +771,15 @@ __global__ __launch_bounds__(NW * 64) void block_gemm_kernel(GemmArgs g) {
                             if (copy_now && i < COPY_GROUPS) dma.issue_part(copy_dst, kb + NSTAGE - 1, i * SUB_N + j);
                             if (head_now) wf[j] = frag_at(next + 16 * j * G_SLICE, w_lo, w_hi);
                             promote(acc[ip][j], p_prev[j], f_prev[j]);
+                            // the four f16 MFMAs interleaved with the promotion FMAs (and, in the
+                            // first block, the tail of the A conversion), two VALU instructions
+                            // after each MFMA (measured: 2% faster than the compiler's own order
+                            // on the outlier shape; 1:1, 1:3 and one pattern per row group were
+                            // not faster)
+                            static_for<4>([&](auto) __device__ __attribute__((always_inline)) {
+                                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+                                __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);   // two VALU
+                            });
                             __builtin_amdgcn_sched_barrier(0);
                         }
                         if (head_now) {
