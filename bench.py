@@ -408,6 +408,66 @@ def backward_measurement(fq, dev, stream, steps: int, warmup: int) -> dict:
     }
 
 
+def bf16_branch_measurement(fq, dev, stream, steps: int, warmup: int) -> dict:
+    """The bf16 branch of linear() on the q down-projection (4096 tokens, 7168 -> 1536): the
+    FP8 weight dequantised by weight_dequant (as the branch does on every call), then the bf16
+    GEMM (bf16 out). torch.matmul on the same bf16 operands is timed beside it as the vendor
+    library's figure for the GEMM alone. Each call is timed by its own event pair."""
+    import numpy as np
+    import torch
+    M, N, K = 4096, 1536, 7168
+    g = torch.Generator(device=dev).manual_seed(3)
+    x = torch.randn((M, K), generator=g, device=dev).to(torch.bfloat16)
+    wq, sw = fq.weight_quant((torch.randn((N, K), generator=g, device=dev) * 0.02).to(torch.bfloat16))
+    wd = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    L = fq._lib
+    sp = stream.cuda_stream
+    calls = [
+        ("weight_dequant", lambda: fq.lib.fp8_weight_dequant(wq.data_ptr(), sw.data_ptr(), wd.data_ptr(), N, K, sp)),
+        ("bf16 GEMM", lambda: fq.lib.fp8_bf16_gemm(x.data_ptr(), wd.data_ptr(), None, y.data_ptr(), L.FP8Q_OUT_BF16,
+                                                   M, N, K, sp)),
+    ]
+
+    def one(ev=None):
+        for i, (name, fn) in enumerate(calls):
+            if ev is not None:
+                ev[i].record(stream)
+            L.check(name, fn())
+        if ev is not None:
+            ev[len(calls)].record(stream)
+
+    for _ in range(warmup):
+        one()
+    evs = [[TimingEvent() for _ in range(len(calls) + 1)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        one(evs[i])
+    torch.cuda.synchronize()
+    t = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(len(calls))] for e in evs]).mean(axis=0) * 1e-3
+    # reference: the vendor library's bf16 GEMM (torch.matmul) on the same operands, same stream
+    wdt = wd.t()
+    with torch.cuda.stream(stream):
+        for _ in range(warmup):
+            torch.matmul(x, wdt, out=y)
+        e0, e1 = TimingEvent(), TimingEvent()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(steps):
+            torch.matmul(x, wdt, out=y)
+        e1.record(stream)
+        torch.cuda.synchronize()
+    t_ref = e0.elapsed_time(e1) * 1e-3 / steps
+    flops = 2.0 * M * N * K
+    return {
+        "workload": "q_down bf16 branch of linear(): weight_dequant 1536x7168, then bf16 GEMM 4096x1536x7168",
+        "us": {name: round(float(v) * 1e6, 3) for (name, _), v in zip(calls, t)},
+        "gemm_tflops": round(flops / float(t[1]) / 1e12, 2),
+        "gemm_frac_of_bf16_peak": round(flops / float(t[1]) / 1e12 / 2500.0, 4),
+        "torch_matmul_us": round(t_ref * 1e6, 3),
+    }
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -618,6 +678,7 @@ def main() -> int:
         # (the part is at its steady clock by now; a shorter warm-up suffices for these)
         result["grouped_gemm"] = grouped_measurement(fq, L, synth, dev, stream, 200, 300)
         result["training_backward"] = backward_measurement(fq, dev, stream, 50, 300)
+        result["bf16_branch"] = bf16_branch_measurement(fq, dev, stream, 50, 100)
 
     if not args.no_cpu_baseline:
         r = min(args.cpu_rows, M) if args.cpu_rows > 0 else cpu_sample_rows(M, N, K)
