@@ -156,6 +156,55 @@ def test_block_gemm_validation(lib):
                 lib.fp8_block_gemm_workspace_bytes(*shape, L.FP8Q_OUT_BF16))
 
 
+def test_bf16_gemm_validation(lib):
+    """fp8_bf16_gemm rejects bad arguments before touching the device (so this runs without
+    one): output dtype, K not a multiple of 64 or at/above 2^23, negative sizes, null and
+    misaligned pointers; an empty output is a no-op."""
+    from fp8_act_quant_amd import _lib as L
+    g = lib.fp8_bf16_gemm
+    ok = dict(x=FAKE, w=FAKE, b=None, y=FAKE, dt=L.FP8Q_OUT_F32, M=4, N=4, K=64)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return g(a["x"], a["w"], a["b"], a["y"], a["dt"], a["M"], a["N"], a["K"], None)
+
+    assert call(dt=7) == L.FP8Q_ERR_DTYPE
+    assert call(K=96) == L.FP8Q_ERR_SHAPE
+    assert call(K=1 << 23) == L.FP8Q_ERR_SHAPE
+    assert call(M=-1) == L.FP8Q_ERR_SHAPE
+    assert call(N=-1) == L.FP8Q_ERR_SHAPE
+    assert call(y=None) == L.FP8Q_ERR_NULL
+    assert call(x=None) == L.FP8Q_ERR_NULL
+    assert call(w=None) == L.FP8Q_ERR_NULL
+    assert call(x=FAKE + 2) == L.FP8Q_ERR_ALIGN
+    assert call(w=FAKE + 8) == L.FP8Q_ERR_ALIGN
+    assert call(y=FAKE + 2) == L.FP8Q_ERR_ALIGN
+    assert call(b=FAKE + 2) == L.FP8Q_ERR_ALIGN
+    assert call(M=0, x=None, w=None, y=None) == L.FP8Q_OK
+    assert call(N=0, x=None, w=None, y=None) == L.FP8Q_OK
+
+
+def test_gemm_split_plans_of_the_workloads(lib):
+    """The split-K plans the GEMM's planner makes for the large workloads, through the
+    host-only workspace query: only the kv down-projection (96 tiles of 128x192 for 256 CUs)
+    splits K, in 2 ranges (32 KiB of arrival words + 2 x 96 fp32 partial tiles of 128x192);
+    fp32 output (exact slices) never splits. The no-allocation entry point refuses, before any
+    launch, a shape whose plan needs more than its static scratch."""
+    from fp8_act_quant_amd import _lib as L
+    ws = lib.fp8_block_gemm_workspace_bytes
+    assert ws(4096, 576, 7168, L.FP8Q_OUT_BF16) == 32768 + 2 * 96 * 128 * 192 * 4
+    for shape in ((4096, 1536, 7168), (8192, 32768, 512), (16384, 7168, 7168), (64, 256, 256)):
+        assert ws(*shape, L.FP8Q_OUT_BF16) == 0, shape
+        assert ws(*shape, L.FP8Q_OUT_F32) == 0, shape
+    assert ws(4096, 576, 7168, L.FP8Q_OUT_F32) == 0
+    assert ws(4096, 576, 7168, L.FP8Q_OUT_BF16) <= L.FP8Q_NOALLOC_SCRATCH_BYTES
+    M, N, K = 4096, 18432, 16384
+    assert ws(M, N, K, L.FP8Q_OUT_BF16) > L.FP8Q_NOALLOC_SCRATCH_BYTES
+    st = lib.fp8_block_gemm_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, L.FP8Q_OUT_BF16, M, N, K, None)
+    assert st == L.FP8Q_ERR_WORKSPACE
+
+
 def test_python_binding_rejects_cpu_tensors_and_bad_shapes():
     import torch
 
