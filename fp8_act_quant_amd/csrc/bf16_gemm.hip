@@ -12,23 +12,27 @@
 // MFMA's A operand and X rows its B operand: lane l of a 16x16 result holds n = 4*(l/16) + r
 // (r = 0..3) for m = l % 16, four consecutive outputs of a row of Y.
 //
-// Tiling. Two tiles: 256 x 256 with 8 waves of 128 x 64 (8 x 4 blocks of 16 x 16) where
-// such tiles fill the 256 CUs, else 128 x 128 with 4 waves of 64 x 64 (two workgroups per
-// CU). K advances in steps of 64 elements, one 128-byte piece of every tile row, copied
-// global -> LDS by LDS-DMA loads (buffer_load ... lds) into one of NSTAGE stage buffers;
-// 16-byte chunks of each row are XOR-swizzled by (row & 7) so that the fragment reads (16
-// rows x 4 chunks per instruction) are free of bank conflicts. Rows past M or N lie outside
-// the loads' buffer range and read as zero.
+// Tiling. Three tiles: 256 x 256 with 8 waves of 128 x 64 (8 x 4 blocks of 16 x 16) for
+// large shapes with long K; 128 x 128 with 4 waves of 64 x 64 (two workgroups per CU); and
+// 64 x 128 with 4 waves of 32 x 64 for shapes with too few 128 x 128 tiles. K advances in
+// steps of 64 elements, one 128-byte piece of every tile row, copied global -> LDS by LDS-DMA
+// loads (buffer_load ... lds) into one of NSTAGE stage buffers; 16-byte chunks of each row
+// are XOR-swizzled by (row & 7) so that the fragment reads (16 rows x 4 chunks per
+// instruction) are free of bank conflicts. Rows past M or N lie outside the loads' buffer
+// range and read as zero.
 //
-// Schedule. 64 x 64 wave tiles: two register sets hold the fragments of two K steps; the
-// MFMAs of step ks take their operands from one set while the other is filled from LDS with
-// step ks + 1, so the LDS reads have a whole step of MFMA work to land behind, and a stage
-// buffer is free once its step is in registers (the copies of step ks + NSTAGE go into the
-// buffer of step ks). 128 x 64 wave tiles (two such sets do not fit beside 128 accumulator
-// registers): the step's W fragments are read first and its A fragments one row group
-// ahead of their MFMAs. Per step a 128 x 64 wave reads 24 KB of fragments for 1024 cycles
-// of MFMA work, a 64 x 64 one 16 KB for 512, which is why the larger tile leads where it
-// fills the GPU.
+// Schedule. 32 x 64 and 64 x 64 wave tiles: two register sets hold the fragments of two K
+// steps; the MFMAs of step ks take their operands from one set while the other is filled
+// from LDS with step ks + 1, so the LDS reads have a whole step of MFMA work to land behind,
+// and a stage buffer is free once its step is in registers (the copies of step ks + NSTAGE
+// go into the buffer of step ks). 128 x 64 wave tiles (two such sets do not fit beside 128
+// accumulator registers): the step's W fragments are read first and its A fragments one row
+// group ahead of their MFMAs. Per step a 128 x 64 wave reads 24 KB of fragments for 1024
+// cycles of MFMA work, a 64 x 64 one 16 KB for 512, which is why the larger tile leads
+// where it fills the GPU and K is long.
+//
+// Epilogue. The output goes through LDS and leaves in 16-byte stores that write whole
+// 128-byte pieces of output rows.
 //
 // Work order. Workgroups are dealt round-robin to the 8 XCDs; the block index is remapped
 // so that each XCD walks a contiguous run of tiles, taken down `group` tile rows per tile
@@ -63,14 +67,39 @@ struct Bf16Tile {
     static constexpr int IPW = A_INSTR + W_INSTR;
     // register prefetch of whole steps where two sets of a step's fragments fit (64 x 64 wave
     // tiles); the 128 x 64 wave tile streams its A fragments through the step instead
-    static constexpr bool PF = WM == 64;
-    static_assert(WAVES_M * WAVES_N == NW && WN == 64 && (WM == 64 || WM == 128), "wave tiles");
+    static constexpr bool PF = WM <= 64;
+    static_assert(WAVES_M * WAVES_N == NW && WN == 64 && (WM == 32 || WM == 64 || WM == 128), "wave tiles");
     static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "copy rows");
     static_assert(STAGE * NSTAGE <= 160 * 1024, "LDS budget");
     static_assert(NSTAGE >= 2 && IPW * (NSTAGE - 1) < 64, "stages");
 };
 using TileXL = Bf16Tile<256, 256, 8, 2, 2>;   // 256 x 256, 8 waves of 128 x 64, 128 KiB of LDS
 using TileS = Bf16Tile<128, 128, 4, 2, 2>;    // 128 x 128, 4 waves, 64 KiB (two workgroups per CU)
+using TileM = Bf16Tile<64, 128, 4, 2, 2>;     // 64 x 128, 4 waves of 32 x 64, 48 KiB
+
+// Output staging of the epilogue: rounds of IPR row groups (RG = 16 x WAVES_M tile rows
+// each) in LDS rows of LDS_ROW bytes, padded so that both the fragment writes and the row
+// reads are free of bank conflicts. BYTES is the LDS the kernel needs for it: the stage
+// buffers, or the whole tile in one round where that fits beside the kernel's occupancy.
+template <class T, int OUT_BF16>
+struct Bf16Epilogue {
+    static constexpr int OB = OUT_BF16 ? 2 : 4;                 // bytes per output element
+    static constexpr int EPC = 16 / OB;                         // elements per 16-byte chunk
+    static constexpr int ROW_WORDS = T::BN * OB / 4;
+    static constexpr int TARGET = OUT_BF16 ? 8 : 16;            // row stride, in banks, mod 64
+    static constexpr int LDS_ROW = 4 * (ROW_WORDS + ((TARGET - ROW_WORDS) % 64 + 64) % 64);
+    static constexpr int RG = T::WAVES_M * 16;
+    static constexpr int CPR = T::BN * OB / 16;                 // 16-byte chunks per output row
+    static constexpr int STAGES = T::STAGE * T::NSTAGE;
+    static constexpr int ALL = T::SUB_M * RG * LDS_ROW;         // the whole tile at once
+    // (the 4-wave tiles run two or more workgroups per CU: their LDS stays within 80 KB)
+    static constexpr int LIMIT = T::NW == 8 ? 160 * 1024 : 80 * 1024;
+    static constexpr bool ONE_ROUND = ALL <= (STAGES > LIMIT ? STAGES : LIMIT);
+    static constexpr int BYTES = ONE_ROUND && ALL > STAGES ? ALL : STAGES;
+    static constexpr int IPR0 = STAGES / (RG * LDS_ROW);
+    static constexpr int IPR = ONE_ROUND ? T::SUB_M : (IPR0 < T::SUB_M ? IPR0 : T::SUB_M);
+    static_assert(IPR >= 1, "epilogue staging does not fit");
+};
 
 struct Bf16GemmArgs {
     const uint16_t *x;
@@ -257,7 +286,7 @@ __global__ __launch_bounds__(NW_ * 64) __attribute__((amdgpu_waves_per_eu(2, 2))
     using T = Bf16Tile<BM_, BN_, NW_, WAVES_M_, NSTAGE_>;
     constexpr int NW = T::NW, WAVES_M = T::WAVES_M, WM = T::WM, WN = T::WN, SUB_M = T::SUB_M, SUB_N = T::SUB_N;
     constexpr int BM = T::BM, BN = T::BN, NSTAGE = T::NSTAGE, IPW = T::IPW;
-    __shared__ __attribute__((aligned(16))) uint8_t smem[T::STAGE * NSTAGE];
+    __shared__ __attribute__((aligned(16))) uint8_t smem[Bf16Epilogue<T, OUT_BF16>::BYTES];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -310,38 +339,68 @@ __global__ __launch_bounds__(NW_ * 64) __attribute__((amdgpu_waves_per_eu(2, 2))
         }
     }
 
-    // epilogue: bias (fp32) added before the output rounding; stores masked to [M, N)
+    // Epilogue, staged through LDS (every wave is past its last fragment read at the first
+    // barrier): IPR row groups of every wave per round are written to LDS as output rows (bias
+    // added in fp32 before the output rounding), then the workgroup stores them 16 bytes per
+    // lane, so that each store instruction writes whole 128-byte pieces of output rows
+    // (stored straight from the fragments, each line would be written in 8- or 16-byte pieces
+    // by four instructions, which costs far more on output-heavy shapes). Stores are masked
+    // to [M, N).
+    {
+        using E = Bf16Epilogue<T, OUT_BF16>;
+        constexpr int OB = E::OB, EPC = E::EPC, LDS_ROW = E::LDS_ROW, RG = E::RG, IPR = E::IPR, CPR = E::CPR;
+        constexpr int NT = NW * 64;
+        const bool vec_ok = ((N * OB) & 15) == 0;   // every output row 16-byte aligned
+        f32x4 bvec[SUB_N];
 #pragma unroll
-    for (int j = 0; j < SUB_N; ++j) {
-        const int64_t n = n0 + wn * WN + 16 * j + 4 * kg;
-        f32x4 b = {0.f, 0.f, 0.f, 0.f};
-        if (g.bias) {
+        for (int j = 0; j < SUB_N; ++j) {
+            bvec[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (g.bias) {
+                const int64_t n = n0 + wn * WN + 16 * j + 4 * kg;
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                if (n + r < N) b[r] = g.bias[n + r];
+                for (int r = 0; r < 4; ++r)
+                    if (n + r < N) bvec[j][r] = g.bias[n + r];
+            }
         }
 #pragma unroll
-        for (int i = 0; i < SUB_M; ++i) {
-            const int64_t m = m0 + wm * WM + 16 * i + frow;
-            if (m >= M || n >= N) continue;
-            const f32x4 v = acc[i][j] + b;
-            if constexpr (OUT_BF16) {
-                uint16_t *yp = reinterpret_cast<uint16_t *>(g.y) + m * N + n;
-                if (n + 4 <= N && (((uintptr_t)yp) & 7) == 0) {
-                    *reinterpret_cast<u32x2 *>(yp) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-                } else {
+        for (int i0 = 0; i0 < SUB_M; i0 += IPR) {
+            __syncthreads();
 #pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        if (n + r < N) yp[r] = (uint16_t)(pack_bf16x2(v[r], 0.f) & 0xFFFF);
+            for (int ii = 0; ii < IPR; ++ii) {
+                if (i0 + ii < SUB_M) {
+                    uint8_t *rowp = smem + (ii * RG + wm * 16 + frow) * LDS_ROW;
+#pragma unroll
+                    for (int j = 0; j < SUB_N; ++j) {
+                        const int col = wn * WN + 16 * j + 4 * kg;
+                        const f32x4 v = acc[i0 + ii][j] + bvec[j];
+                        if constexpr (OUT_BF16)
+                            *reinterpret_cast<u32x2 *>(rowp + col * 2) =
+                                u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+                        else
+                            *reinterpret_cast<f32x4 *>(rowp + col * 4) = v;
+                    }
                 }
-            } else {
-                float *yp = reinterpret_cast<float *>(g.y) + m * N + n;
-                if (n + 4 <= N && (((uintptr_t)yp) & 15) == 0) {
-                    *reinterpret_cast<f32x4 *>(yp) = v;
+            }
+            __syncthreads();
+            const int groups = (SUB_M - i0) < IPR ? (SUB_M - i0) : IPR;   // a constant once unrolled
+            const int chunks = groups * RG * CPR;
+            for (int c = threadIdx.x; c < chunks; c += NT) {
+                const int r = c / CPR, cb = c - r * CPR;
+                const int ii = r / RG, within = r - ii * RG;
+                const int64_t m = m0 + (within >> 4) * WM + 16 * (i0 + ii) + (within & 15);
+                const int64_t n = n0 + cb * EPC;
+                if (m >= M || n >= N) continue;
+                const uint8_t *src = smem + r * LDS_ROW + cb * 16;
+                uint8_t *yp = reinterpret_cast<uint8_t *>(g.y) + (m * N + n) * OB;
+                if (vec_ok && n + EPC <= N) {
+                    *reinterpret_cast<u32x4 *>(yp) = *reinterpret_cast<const u32x4 *>(src);
                 } else {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        if (n + r < N) yp[r] = v[r];
+                    for (int e = 0; e < EPC && n + e < N; ++e) {
+                        if constexpr (OUT_BF16)
+                            reinterpret_cast<uint16_t *>(yp)[e] = reinterpret_cast<const uint16_t *>(src)[e];
+                        else
+                            reinterpret_cast<float *>(yp)[e] = reinterpret_cast<const float *>(src)[e];
+                    }
                 }
             }
         }
@@ -385,14 +444,19 @@ hipError_t launch_bf16_gemm(const uint16_t *x, const uint16_t *w, const float *b
                             int64_t N, int64_t K, hipStream_t stream) {
     if (M == 0 || N == 0) return hipSuccess;
     Bf16GemmArgs a{x, w, bias, y, M, N, K, 0, 0, 1};
-    // the 256 x 256 tile where its tiles fill the 256 CUs, else the 128 x 128 one (two
-    // workgroups per CU); FP8Q_BF16_TILE=256x256 or 128x128 forces one (tuning and tests)
+    // FP8Q_BF16_TILE=256x256, 128x128 or 64x128 forces a tile (tuning and tests). Otherwise
+    // (measured on MI355X): 64x128 where 128x128 tiles would not give every CU more than one;
+    // 256x256 where its tiles fill the 256 CUs and K is long enough (K >= 2048) for its
+    // per-tile cost to pay off; else 128x128, two workgroups per CU.
     if (const char *e = std::getenv("FP8Q_BF16_TILE")) {
         if (std::strcmp(e, "256x256") == 0) return launch_tile<TileXL>(a, out_bf16, stream);
         if (std::strcmp(e, "128x128") == 0) return launch_tile<TileS>(a, out_bf16, stream);
+        if (std::strcmp(e, "64x128") == 0) return launch_tile<TileM>(a, out_bf16, stream);
     }
+    const int64_t s_tiles = ((M + TileS::BM - 1) / TileS::BM) * ((N + TileS::BN - 1) / TileS::BN);
     const int64_t xl_tiles = ((M + TileXL::BM - 1) / TileXL::BM) * ((N + TileXL::BN - 1) / TileXL::BN);
-    if (xl_tiles >= 256) return launch_tile<TileXL>(a, out_bf16, stream);
+    if (s_tiles <= 256) return launch_tile<TileM>(a, out_bf16, stream);
+    if (xl_tiles >= 256 && K >= 2048) return launch_tile<TileXL>(a, out_bf16, stream);
     return launch_tile<TileS>(a, out_bf16, stream);
 }
 

@@ -275,8 +275,8 @@ size_t fp8_block_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int y_dty
 /* The same choice can be made for a whole process through the environment, read once at
  * the first GEMM call: FP8Q_GEMM_TILE=<configuration name> and FP8Q_GEMM_SPLITS=<count>.
  * FP8Q_AQ_WGS_PER_CU=<1..32> sets fp8_act_quant's resident workgroups per CU (default 16).
- * FP8Q_BF16_TILE=256x256 or 128x128 pins fp8_bf16_gemm's tile (read at every call; by
- * default the 256x256 tile where it has at least 256 tiles, else 128x128). */
+ * FP8Q_BF16_TILE=256x256, 128x128 or 64x128 pins fp8_bf16_gemm's tile (read at every call;
+ * by default chosen from the shape). */
 int fp8q_gemm_force_config(int config, int splits);
 const char *fp8q_gemm_config_name(int config);
 

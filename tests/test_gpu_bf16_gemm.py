@@ -52,7 +52,7 @@ def test_bf16_gemm_large_tile_every_output(K, out):
     assert res["violations"] == 0 and res["strict_violations"] == 0, res
 
 
-@pytest.mark.parametrize("tile", ["256x256", "128x128"])
+@pytest.mark.parametrize("tile", ["256x256", "128x128", "64x128"])
 @pytest.mark.parametrize("M,N,K", [(1, 1, 64), (300, 260, 448), (513, 129, 1024), (257, 511, 128)])
 def test_bf16_gemm_each_tile_every_output(tile, M, N, K, monkeypatch):
     """Each tile forced (FP8Q_BF16_TILE) on small ragged shapes, both output dtypes, with a
