@@ -350,7 +350,8 @@ __global__ __launch_bounds__(NW_ * 64) __attribute__((amdgpu_waves_per_eu(2, 2))
         using E = Bf16Epilogue<T, OUT_BF16>;
         constexpr int OB = E::OB, EPC = E::EPC, LDS_ROW = E::LDS_ROW, RG = E::RG, IPR = E::IPR, CPR = E::CPR;
         constexpr int NT = NW * 64;
-        const bool vec_ok = ((N * OB) & 15) == 0;   // every output row 16-byte aligned
+        // every output row 16-byte aligned (the interface asks only 4-byte alignment of y)
+        const bool vec_ok = ((N * OB) & 15) == 0 && (reinterpret_cast<uintptr_t>(g.y) & 15) == 0;
         f32x4 bvec[SUB_N];
 #pragma unroll
         for (int j = 0; j < SUB_N; ++j) {

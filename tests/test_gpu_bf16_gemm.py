@@ -69,6 +69,35 @@ def test_bf16_gemm_each_tile_every_output(tile, M, N, K, monkeypatch):
         assert res["violations"] == 0, res
 
 
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_bf16_gemm_output_4_byte_aligned(out):
+    """The interface asks only 4-byte alignment of y: an output 4 bytes past a 16-byte
+    boundary (so no row of it is 16-byte aligned), through the C ABI, on every output."""
+    from fp8_act_quant_amd import _lib as L
+    M, N, K = 300, 264, 192
+    X = synth.random_bf16((M, K), seed=41)
+    W = synth.random_bf16((N, K), seed=42, std=0.02)
+    x, w = dev_bf16(X), dev_bf16(W)
+    dt = torch.float32 if out == "f32" else torch.bfloat16
+    per = 1 if out == "f32" else 2                    # elements in 4 bytes
+    buf = torch.zeros(M * N + 8 * per, dtype=dt, device="cuda")
+    assert buf.data_ptr() % 16 == 0
+    y = buf[per:per + M * N].view(M, N)
+    assert y.data_ptr() % 16 == 4
+    code = L.FP8Q_OUT_F32 if out == "f32" else L.FP8Q_OUT_BF16
+    for tile in ("256x256", "128x128", "64x128"):
+        import os
+        os.environ["FP8Q_BF16_TILE"] = tile
+        try:
+            assert fq.lib.fp8_bf16_gemm(x.data_ptr(), w.data_ptr(), None, y.data_ptr(), code, M, N, K, None) == 0
+            torch.cuda.synchronize()
+        finally:
+            del os.environ["FP8Q_BF16_TILE"]
+        res = check_bf16_linear_every_output(y, X, W, out, f"bf16 gemm 4-byte aligned y {tile} {out}")
+        assert res["violations"] == 0 and res["strict_violations"] == 0, (tile, res)
+        assert torch.count_nonzero(buf[:per]) == 0 and torch.count_nonzero(buf[per + M * N:]) == 0
+
+
 def test_bf16_gemm_k_zero_is_bias_and_empty_m():
     x = torch.empty((5, 0), dtype=torch.bfloat16, device="cuda")
     w = torch.empty((7, 0), dtype=torch.bfloat16, device="cuda")
