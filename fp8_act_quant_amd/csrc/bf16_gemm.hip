@@ -65,8 +65,9 @@ struct Bf16Tile {
     static constexpr int STAGE = A_BYTES + W_BYTES;
     static constexpr int A_INSTR = BM / (8 * NW), W_INSTR = BN / (8 * NW);   // 1 KiB copies per wave and stage
     static constexpr int IPW = A_INSTR + W_INSTR;
-    // register prefetch of whole steps where two sets of a step's fragments fit (64 x 64 wave
-    // tiles); the 128 x 64 wave tile streams its A fragments through the step instead
+    // register prefetch of whole steps where two sets of a step's fragments fit (wave tiles
+    // of 32 x 64 and 64 x 64); the 128 x 64 wave tile streams its A fragments through the
+    // step instead
     static constexpr bool PF = WM <= 64;
     static_assert(WAVES_M * WAVES_N == NW && WN == 64 && (WM == 32 || WM == 64 || WM == 128), "wave tiles");
     static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "copy rows");
