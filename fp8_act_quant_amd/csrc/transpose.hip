@@ -42,7 +42,10 @@ __global__ __launch_bounds__(AQT_THREADS) void act_quant_t_kernel(const uint16_t
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
         const int64_t m = tok0 + r;
-        row[r] = (chunk_ok && m < M) ? __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(x + m * C + c0))
+        // (ordinary loads: a load instruction takes 64 bytes of each of 16 rows, and the
+        // rest of each line, loaded by another wave, is then found in the L2; non-temporal
+        // loads cost 27.0 against 20.2 us on a 4096 x 7168 input)
+        row[r] = (chunk_ok && m < M) ? *reinterpret_cast<const u32x4 *>(x + m * C + c0)
                                      : u32x4{0, 0, 0, 0};
     }
     // col[e]: channel c0 + e over the 8 tokens, as 8 bf16 in token order (2 per word)
