@@ -4,8 +4,8 @@ through the C ABI.
 Expert e's rows of the output are its own block-scaled GEMM, so the oracle is the pinned
 block GEMM applied per expert. Small ragged groupings (empty experts, experts of one row,
 of exactly one tile, of one tile plus one row) are compared on every output in both
-contraction modes; the routed down-projection at full size on seeded samples that include
-every expert's first and last row. Tolerances as for the plain GEMM (tests/helpers.py).
+contraction modes, and so is the routed down-projection at full size, expert by expert.
+Tolerances as for the plain GEMM (tests/helpers.py).
 """
 import numpy as np
 import pytest
