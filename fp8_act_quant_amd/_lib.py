@@ -50,6 +50,7 @@ SIGNATURES = {
     "fp8_rowwise_gemm_workspace_bytes": (ctypes.c_size_t, [_I64, _I64, _I64, ctypes.c_int]),
     "fp8q_gemm_force_config": (ctypes.c_int, [ctypes.c_int, ctypes.c_int]),
     "fp8q_gemm_config_name": (ctypes.c_char_p, [ctypes.c_int]),
+    "fp8q_gemm_plan": (ctypes.c_int, [_I64, _I64, _I64, ctypes.c_int, _P, _P]),
     "fp8q_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "fp8q_version": (ctypes.c_int, []),
 }

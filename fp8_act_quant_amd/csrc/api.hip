@@ -275,6 +275,19 @@ int fp8q_gemm_force_config(int config, int splits) {
 
 const char *fp8q_gemm_config_name(int config) { return fp8q::gemm_config_name(config); }
 
+int fp8q_gemm_plan(int64_t M, int64_t N, int64_t K, int y_dtype, int *config, int *splits) {
+    if (!config || !splits) return FP8Q_ERR_NULL;
+    const int dtype = y_dtype & 0xFF;
+    const int mode = y_dtype & ~0xFF & ~FP8Q_SA_KMAJOR;   // (the scale layout does not change the plan)
+    if (dtype != FP8Q_OUT_F32 && dtype != FP8Q_OUT_BF16) return FP8Q_ERR_DTYPE;
+    if (mode != 0 && mode != FP8Q_GEMM_FP8_PRODUCTS && mode != FP8Q_GEMM_EXACT_SLICES) return FP8Q_ERR_DTYPE;
+    if (M <= 0 || N <= 0 || K <= 0 || (K % kBlock) != 0 || K > kMaxGemmK) return FP8Q_ERR_SHAPE;
+    if (N > kMaxElems / M || shape_ok(M, K) || shape_ok(N, K)) return FP8Q_ERR_SHAPE;
+    const bool exact = mode == FP8Q_GEMM_EXACT_SLICES || (mode == 0 && dtype == FP8Q_OUT_F32);
+    fp8q::gemm_plan(M, N, K, dtype == FP8Q_OUT_BF16, exact, config, splits);
+    return FP8Q_OK;
+}
+
 const char *fp8q_strerror(int status) {
     switch (status) {
     case FP8Q_OK: return "ok";
@@ -291,6 +304,6 @@ const char *fp8q_strerror(int status) {
     }
 }
 
-int fp8q_version(void) { return (1 << 16) | 4; }
+int fp8q_version(void) { return (1 << 16) | 5; }
 
 }  // extern "C"

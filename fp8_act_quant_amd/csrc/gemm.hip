@@ -1167,6 +1167,13 @@ static GemmPlan make_plan(int64_t M, int64_t N, int64_t K, bool exact, size_t ws
     return best;
 }
 
+void gemm_plan(int64_t M, int64_t N, int64_t K, bool, bool exact, int *tile, int *splits) {
+    const GemmPlan p = make_plan(M, N, K, exact, 0, true);
+    // (what dispatch launches: a forced tile the exact-slice mode lacks runs as 128x128)
+    *tile = exact && !kTiles[p.tile].exact_ok ? (int)T128x128 : p.tile;
+    *splits = p.splits;
+}
+
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, bool, bool exact, bool rowb) {
     return split_bytes(make_plan(M, N, K, exact, 0, true, rowb));
 }

@@ -66,5 +66,8 @@ hipError_t launch_grouped_gemm(const uint8_t *aq, const float *sa, const uint8_t
 // tuning / test hook: force a tile configuration (-1: planner) and split count (0: planner)
 bool gemm_force_config(int tile, int splits);
 const char *gemm_config_name(int tile);
+// the tile configuration and split count launch_block_gemm picks for a shape, given a
+// workspace of at least gemm_workspace_bytes
+void gemm_plan(int64_t M, int64_t N, int64_t K, bool out_bf16, bool exact, int *tile, int *splits);
 
 }  // namespace fp8q

@@ -271,7 +271,12 @@ size_t fp8_block_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int y_dty
  * implement falls back to its default configuration. Returns FP8Q_ERR_SHAPE for values out
  * of range. Process-wide and not synchronised with calls in flight on other threads.
  * fp8q_gemm_config_name(config) names a configuration ("256x256w8": BM x BN, w8 = 8
- * waves, s2 = two stages), or returns NULL past the last one. */
+ * waves, s2 = two stages), or returns NULL past the last one.
+ * fp8q_gemm_plan(M, N, K, y_dtype, &config, &splits) reports the configuration and split count
+ * fp8_block_gemm would use for that shape and y_dtype (the same flags) when given a workspace
+ * of at least fp8_block_gemm_workspace_bytes, forced choices included. Returns FP8Q_OK, or
+ * FP8Q_ERR_NULL / FP8Q_ERR_DTYPE / FP8Q_ERR_SHAPE (M, N, K must be positive) without writing
+ * the outputs. */
 /* The same choice can be made for a whole process through the environment, read once at
  * the first GEMM call: FP8Q_GEMM_TILE=<configuration name> and FP8Q_GEMM_SPLITS=<count>.
  * FP8Q_AQ_WGS_PER_CU=<1..32> sets fp8_act_quant's resident workgroups per CU (default 16).
@@ -279,6 +284,7 @@ size_t fp8_block_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int y_dty
  * by default chosen from the shape). */
 int fp8q_gemm_force_config(int config, int splits);
 const char *fp8q_gemm_config_name(int config);
+int fp8q_gemm_plan(int64_t M, int64_t N, int64_t K, int y_dtype, int *config, int *splits);
 
 /* Static string describing a status code (never NULL). */
 const char *fp8q_strerror(int status);

@@ -205,6 +205,45 @@ def test_gemm_split_plans_of_the_workloads(lib):
     assert st == L.FP8Q_ERR_WORKSPACE
 
 
+def test_gemm_plans_of_the_workloads(lib):
+    """fp8q_gemm_plan reports the planner's choice for a shape (host only), the same one
+    fp8_block_gemm_workspace_bytes sizes: the configurations and split counts of the large
+    workloads in their default modes; a forced configuration that the contraction mode does
+    not implement leaves the default; bad arguments are rejected without writing the outputs."""
+    from fp8_act_quant_amd import _lib as L
+    names = []
+    while (n := lib.fp8q_gemm_config_name(len(names))) is not None:
+        names.append(n.decode())
+
+    def plan(M, N, K, dt):
+        c, s = ctypes.c_int(-7), ctypes.c_int(-7)
+        assert lib.fp8q_gemm_plan(M, N, K, dt, ctypes.byref(c), ctypes.byref(s)) == L.FP8Q_OK
+        return names[c.value], s.value
+
+    bf16, f32 = L.FP8Q_OUT_BF16, L.FP8Q_OUT_F32
+    assert plan(4096, 1536, 7168, bf16) == ("128x192w8", 1)
+    assert plan(4096, 1536, 7168, bf16 | L.FP8Q_SA_KMAJOR) == ("128x192w8", 1)
+    assert plan(4096, 576, 7168, bf16) == ("128x192w8", 2)
+    assert plan(4096, 576, 7168, f32) == ("128x128", 1)
+    assert plan(8192, 32768, 512, bf16) == ("256x256w8", 1)
+    assert plan(16384, 7168, 7168, f32) == ("256x128w8", 1)
+    assert plan(16384, 7168, 7168, f32 | L.FP8Q_GEMM_FP8_PRODUCTS) == ("256x256w8", 1)
+    try:
+        assert lib.fp8q_gemm_force_config(names.index("256x256w8"), 0) == L.FP8Q_OK
+        assert plan(4096, 1536, 7168, bf16)[0] == "256x256w8"      # (split count: the planner's)
+        assert plan(4096, 1536, 7168, f32) == ("128x128", 1)      # no exact-slice 256x256: the default
+        assert lib.fp8q_gemm_force_config(names.index("256x256w8"), 1) == L.FP8Q_OK
+        assert plan(4096, 1536, 7168, bf16) == ("256x256w8", 1)
+    finally:
+        lib.fp8q_gemm_force_config(-1, 0)
+    c, s = ctypes.c_int(-7), ctypes.c_int(-7)
+    for args, err in (((0, 8, 128, bf16), L.FP8Q_ERR_SHAPE), ((8, 8, 100, bf16), L.FP8Q_ERR_SHAPE),
+                      ((8, 8, 128, 3), L.FP8Q_ERR_DTYPE)):
+        assert lib.fp8q_gemm_plan(*args, ctypes.byref(c), ctypes.byref(s)) == err, args
+    assert lib.fp8q_gemm_plan(8, 8, 128, bf16, None, ctypes.byref(s)) == L.FP8Q_ERR_NULL
+    assert (c.value, s.value) == (-7, -7)
+
+
 def test_python_binding_rejects_cpu_tensors_and_bad_shapes():
     import torch
 

@@ -463,6 +463,13 @@ def test_gemm_kmajor_scales_bias_and_errors():
                                    None) == L.FP8Q_ERR_DTYPE
 
 
+def _plan(M, N, K, y_dtype):
+    import ctypes
+    c, s = ctypes.c_int(-1), ctypes.c_int(-1)
+    assert fq.lib.fp8q_gemm_plan(M, N, K, y_dtype, ctypes.byref(c), ctypes.byref(s)) == 0
+    return fq.lib.fp8q_gemm_config_name(c.value).decode(), s.value
+
+
 @pytest.mark.parametrize("name", ["q_down", "kv_down", "kv_up", "outlier"])
 def test_gemm_workload_full_size_every_output(name):
     """Each large workload at full size, in the benchmark's launch (K-block-major activation
@@ -493,9 +500,10 @@ def test_gemm_workload_full_size_every_output(name):
 
 
 def test_gemm_full_size_repeat_bitwise():
-    """Repeated launches at full size give identical bits, on the two paths the q_down
-    repeat does not take: kv_down's split-K schedule (two K ranges, partials exchanged through
-    the automatic workspace) and the outlier shape's exact-slice contraction. kv_down runs A1,
+    """Repeated launches at full size give identical bits, on the paths the q_down repeat
+    does not take: kv_down's split-K schedule (two K ranges, partials exchanged through the
+    automatic workspace), the KV up-projection's many rounds of 256x256 tiles and the outlier
+    shape's exact-slice contraction. kv_down runs A1,
     then A2 through the same workspace, then A1 again: the two A1 results must be identical
     and the A2 result must meet the bound on every output."""
     g = torch.Generator(device="cuda").manual_seed(31)
@@ -513,6 +521,15 @@ def test_gemm_full_size_repeat_bitwise():
                              sw.cpu().numpy(), "bf16", "kv_down second input")
     assert res["violations"] == 0 and res["strict_violations"] == 0, res
     del y1, y2, y1b, aq1, aq2
+    # the KV up-projection: 256x256 tiles, 16 rounds of them
+    M, N, K = 8192, 32768, 512
+    assert _plan(M, N, K, 1) == ("256x256w8", 1)
+    aq, sa = fq.act_quant(torch.randn((M, K), generator=g, device="cuda").to(torch.bfloat16), scale_layout="kmajor")
+    wq, sw = fq.weight_quant((torch.randn((N, K), generator=g, device="cuda") * 0.02).to(torch.bfloat16))
+    ys = [fq.fp8_gemm(aq, sa, wq, sw).view(torch.int16) for _ in range(3)]
+    torch.cuda.synchronize()
+    assert all(torch.equal(ys[0], y) for y in ys[1:]), [int((ys[0] != y).sum()) for y in ys[1:]]
+    del ys, aq, sa, wq, sw
     M, N, K = 16384, 7168, 7168
     aq, sa = fq.act_quant(torch.randn((M, K), generator=g, device="cuda").to(torch.bfloat16), scale_layout="kmajor")
     wq, sw = fq.weight_quant((torch.randn((N, K), generator=g, device="cuda") * 0.02).to(torch.bfloat16))
