@@ -104,6 +104,32 @@ class TimingEvent:
             self._hip.hipEventDestroy(self.h)
 
 
+def device_info(dev) -> dict:
+    """The GPU's CU count and peak engine clock (HIP device attributes) and the dense matrix
+    peaks they give: per CU and clock, 8192 FP8 and 4096 f16/bf16 flops (4 SIMDs, one 16x16x128
+    FP8 or 16x16x32 f16 MFMA per 32 or 16 cycles each). The loaded clock of long GEMMs is lower
+    (the part is power-limited), so these are ceilings; `peak` in the line is the datasheet one."""
+    import ctypes
+
+    import torch
+    hip = TimingEvent._runtime()
+    hip.hipDeviceGetAttribute.argtypes = [ctypes.POINTER(ctypes.c_int), ctypes.c_int, ctypes.c_int]
+    CLOCK_RATE_KHZ, MULTIPROCESSOR_COUNT = 5, 63   # hipDeviceAttribute_t values (hip_runtime_api.h)
+    vals = {}
+    for key, attr in (("clock_khz", CLOCK_RATE_KHZ), ("cus", MULTIPROCESSOR_COUNT)):
+        v = ctypes.c_int()
+        rc = hip.hipDeviceGetAttribute(ctypes.byref(v), attr, dev.index or 0)
+        vals[key] = v.value if rc == 0 else None
+    props = torch.cuda.get_device_properties(dev)
+    info = {"name": props.name, "arch": props.gcnArchName, "cus": vals["cus"],
+            "max_clock_mhz": vals["clock_khz"] // 1000 if vals["clock_khz"] else None}
+    if vals["cus"] and vals["clock_khz"]:
+        ghz = vals["clock_khz"] / 1e6
+        info["fp8_dense_tflops_at_max_clock"] = round(vals["cus"] * 8192 * ghz / 1e3, 1)
+        info["f16_dense_tflops_at_max_clock"] = round(vals["cus"] * 4096 * ghz / 1e3, 1)
+    return info
+
+
 def kernel_source_sha() -> str:
     h = hashlib.sha256()
     for p in GEMM_SOURCES:
@@ -672,6 +698,7 @@ def main() -> int:
             "back_to_back_frac_of_copy": round(aq_bytes / t_aq_b2b / 1e9 / copy_ref["gbs"], 4),
         },
         "gemm_only_tflops": round(gemm_tflops, 2),
+        "device": device_info(dev),
     }
 
     if not args.no_extras and not args.calibrate_copy:   # (counter runs: the calibration kernel must be the only multiply)
