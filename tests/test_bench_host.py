@@ -125,3 +125,19 @@ def test_cpu_sample_is_bounded():
 def test_host_cpu_fields():
     h = bench.host_cpu()
     assert h["nproc"] >= 1 and h["cpu_count"] >= h["nproc"]
+
+
+def test_committed_counters_are_of_the_current_gemm_source():
+    """Every committed counter summary (the MFMA-busy and traffic figures bench.py reports)
+    was taken on the GEMM source as it is now: its stored hash is the current one, and so is
+    the hash the markdown summaries of the same collection name. A change to the GEMM source
+    without a new collection fails here instead of leaving bench.py to report nulls."""
+    sha = bench.kernel_source_sha()
+    for wl in ("outlier", "kv_up", "kv_down", "q_down"):
+        for path in (bench.traffic_file(wl), bench.mfma_file(wl)):
+            with open(path) as f:
+                assert json.load(f)["kernel_source_sha"] == sha, path
+    for name in ("gemm_workloads_counters.md", "gemm_workloads_kernel_trace.md", "bench_outlier_kernel_trace.md",
+                 "gemm_outlier_issue_counters.md"):
+        with open(os.path.join(ROOT, "profiles", name)) as f:
+            assert f"`{sha}`" in f.read(), name
