@@ -121,8 +121,10 @@ def device_info(dev) -> dict:
         rc = hip.hipDeviceGetAttribute(ctypes.byref(v), attr, dev.index or 0)
         vals[key] = v.value if rc == 0 else None
     props = torch.cuda.get_device_properties(dev)
-    info = {"name": props.name, "arch": props.gcnArchName, "cus": vals["cus"],
+    info = {"arch": props.gcnArchName, "cus": vals["cus"],
             "max_clock_mhz": vals["clock_khz"] // 1000 if vals["clock_khz"] else None}
+    if props.name:
+        info["name"] = props.name
     if vals["cus"] and vals["clock_khz"]:
         ghz = vals["clock_khz"] / 1e6
         info["fp8_dense_tflops_at_max_clock"] = round(vals["cus"] * 8192 * ghz / 1e3, 1)
