@@ -86,8 +86,8 @@ MOE_WORKLOADS = {
         MoEWorkload("moe_small", 512, 64, 6, 6, 300, 512, "bf16",
                     "small routed-expert GEMM: 6 local experts, ragged N"),
         MoEWorkload("moe_down", 8192, 256, 8, 32, 7168, 2048, "bf16",
-                    "routed experts' down-projection 2048 -> 7168, 32 of 256 experts (one GPU of 8), "
-                    "8192 tokens top-8"),
+                    "routed experts' down-projection 2048 -> 7168 (expert hidden size 2048 assumed: the pages "
+                    "give none), 32 of 256 experts (one GPU of 8), 8192 tokens top-8"),
     ]
 }
 
