@@ -31,6 +31,10 @@ constexpr int64_t kBf16Step = 64;
 constexpr int64_t kMaxBf16K = ((int64_t)1 << 23) - kBf16Step;
 // K-block-major activation scales are addressed with 32-bit byte offsets: M * K/128 < 2^29
 constexpr int64_t kMaxKmajorScales = (int64_t)1 << 29;
+// The GEMMs count tile rows and columns in 32-bit ints (64-row tiles at the smallest), and a
+// grid holds at most 2^32 / 256 workgroups; with M, N <= 2^36 the counts stay far inside
+// both. (No device holds such an operand: 2^36 rows of K >= 64 elements.)
+constexpr int64_t kMaxGemmRows = (int64_t)1 << 36;
 
 bool misaligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
 
@@ -120,7 +124,7 @@ int fp8_block_gemm_bias(const uint8_t *aq, const float *sa, const uint8_t *wq, c
     if (int e = shape_ok(M, K)) return e;
     if (int e = shape_ok(N, K)) return e;
     if (M > 0 && N > kMaxElems / M) return FP8Q_ERR_SHAPE;
-    if (K > kMaxGemmK) return FP8Q_ERR_SHAPE;
+    if (K > kMaxGemmK || M > kMaxGemmRows || N > kMaxGemmRows) return FP8Q_ERR_SHAPE;
     if (sa_kmajor && K > 0 && M >= kMaxKmajorScales / (K / kBlock)) return FP8Q_ERR_SHAPE;
     if (M == 0 || N == 0) return FP8Q_OK;
     if (!y) return FP8Q_ERR_NULL;
@@ -142,6 +146,7 @@ int fp8_bf16_gemm(const uint16_t *x, const uint16_t *w, const float *bias, void 
     if (y_dtype != FP8Q_OUT_F32 && y_dtype != FP8Q_OUT_BF16) return FP8Q_ERR_DTYPE;
     if (M < 0 || N < 0 || K < 0 || (K % kBf16Step) != 0 || K > kMaxBf16K) return FP8Q_ERR_SHAPE;
     if ((K > 0 && (M > kMaxElems / K || N > kMaxElems / K)) || (M > 0 && N > kMaxElems / M)) return FP8Q_ERR_SHAPE;
+    if (M > kMaxGemmRows || N > kMaxGemmRows) return FP8Q_ERR_SHAPE;
     if (M == 0 || N == 0) return FP8Q_OK;
     if (!y || (K > 0 && (!x || !w))) return FP8Q_ERR_NULL;
     if (misaligned(x, 16) || misaligned(w, 16) || misaligned(y, 4) || misaligned(bias, 4)) return FP8Q_ERR_ALIGN;
@@ -161,7 +166,7 @@ int fp8_block_gemm_noalloc(const uint8_t *aq, const float *sa, const uint8_t *wq
     if (int e = shape_ok(M, K)) return e;
     if (int e = shape_ok(N, K)) return e;
     if (M > 0 && N > kMaxElems / M) return FP8Q_ERR_SHAPE;
-    if (K > kMaxGemmK) return FP8Q_ERR_SHAPE;
+    if (K > kMaxGemmK || M > kMaxGemmRows || N > kMaxGemmRows) return FP8Q_ERR_SHAPE;
     if (sa_kmajor && K > 0 && M >= kMaxKmajorScales / (K / kBlock)) return FP8Q_ERR_SHAPE;
     if (M == 0 || N == 0) return FP8Q_OK;
     const bool exact = mode == FP8Q_GEMM_EXACT_SLICES || (mode == 0 && dtype == FP8Q_OUT_F32);
@@ -189,7 +194,7 @@ int fp8_grouped_gemm(const uint8_t *aq, const float *sa, const uint8_t *wq, cons
     if (N > 0 && experts > kMaxElems / N) return FP8Q_ERR_SHAPE;
     if (int e = shape_ok(experts * N, K)) return e;
     if (rows > 0 && N > kMaxElems / rows) return FP8Q_ERR_SHAPE;
-    if (K > kMaxGemmK || rows > INT32_MAX / 2) return FP8Q_ERR_SHAPE;
+    if (K > kMaxGemmK || rows > INT32_MAX / 2 || N > kMaxGemmRows) return FP8Q_ERR_SHAPE;
     if (rows == 0 || N == 0) return FP8Q_OK;
     if (!y || !offsets) return FP8Q_ERR_NULL;
     if (K > 0 && (!aq || !sa || !wq || !sw)) return FP8Q_ERR_NULL;
@@ -233,7 +238,7 @@ int fp8_rowwise_gemm(const uint8_t *aq, const float *sa, const uint8_t *bq, cons
     if (int e = shape_ok(M, K)) return e;
     if (int e = shape_ok(N, K)) return e;
     if (M > 0 && N > kMaxElems / M) return FP8Q_ERR_SHAPE;
-    if (K > kMaxGemmK) return FP8Q_ERR_SHAPE;
+    if (K > kMaxGemmK || M > kMaxGemmRows || N > kMaxGemmRows) return FP8Q_ERR_SHAPE;
     if (M == 0 || N == 0) return FP8Q_OK;
     if (!y) return FP8Q_ERR_NULL;
     if (K > 0 && (!aq || !sa || !bq || !sb)) return FP8Q_ERR_NULL;
@@ -249,7 +254,7 @@ int fp8_rowwise_gemm(const uint8_t *aq, const float *sa, const uint8_t *bq, cons
 
 size_t fp8_rowwise_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int y_dtype) {
     if (M <= 0 || N <= 0 || K <= 0 || (K % kBlock) != 0 || K > kMaxGemmK) return 0;
-    if (N > kMaxElems / M || shape_ok(M, K) || shape_ok(N, K)) return 0;
+    if (N > kMaxElems / M || shape_ok(M, K) || shape_ok(N, K) || M > kMaxGemmRows || N > kMaxGemmRows) return 0;
     const int dtype = y_dtype & 0xFF;
     const int mode = y_dtype & ~0xFF;
     if (dtype != FP8Q_OUT_F32 && dtype != FP8Q_OUT_BF16) return 0;
@@ -260,7 +265,7 @@ size_t fp8_rowwise_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int y_d
 
 size_t fp8_block_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int y_dtype) {
     if (M <= 0 || N <= 0 || K <= 0 || (K % kBlock) != 0 || K > kMaxGemmK) return 0;
-    if (N > kMaxElems / M || shape_ok(M, K) || shape_ok(N, K)) return 0;
+    if (N > kMaxElems / M || shape_ok(M, K) || shape_ok(N, K) || M > kMaxGemmRows || N > kMaxGemmRows) return 0;
     const int dtype = y_dtype & 0xFF;
     const int mode = y_dtype & ~0xFF & ~FP8Q_SA_KMAJOR;   // (the scale layout does not change the plan)
     if (dtype != FP8Q_OUT_F32 && dtype != FP8Q_OUT_BF16) return 0;
@@ -282,7 +287,8 @@ int fp8q_gemm_plan(int64_t M, int64_t N, int64_t K, int y_dtype, int *config, in
     if (dtype != FP8Q_OUT_F32 && dtype != FP8Q_OUT_BF16) return FP8Q_ERR_DTYPE;
     if (mode != 0 && mode != FP8Q_GEMM_FP8_PRODUCTS && mode != FP8Q_GEMM_EXACT_SLICES) return FP8Q_ERR_DTYPE;
     if (M <= 0 || N <= 0 || K <= 0 || (K % kBlock) != 0 || K > kMaxGemmK) return FP8Q_ERR_SHAPE;
-    if (N > kMaxElems / M || shape_ok(M, K) || shape_ok(N, K)) return FP8Q_ERR_SHAPE;
+    if (N > kMaxElems / M || shape_ok(M, K) || shape_ok(N, K) || M > kMaxGemmRows || N > kMaxGemmRows)
+        return FP8Q_ERR_SHAPE;
     const bool exact = mode == FP8Q_GEMM_EXACT_SLICES || (mode == 0 && dtype == FP8Q_OUT_F32);
     fp8q::gemm_plan(M, N, K, dtype == FP8Q_OUT_BF16, exact, config, splits);
     return FP8Q_OK;

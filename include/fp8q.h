@@ -136,7 +136,7 @@ int fp8_weight_dequant(const uint8_t *q, const float *s, uint16_t *w, int64_t N,
  *   y  [M, N] output, fp32 (y_dtype = FP8Q_OUT_F32) or bf16 bits (FP8Q_OUT_BF16, RNE of
  *      the fp32 accumulator). With K = 0 the output is all zeros.
  *   aq, wq, y: 16-byte aligned; sa, sw: 4-byte aligned. M, N >= 0 arbitrary (ragged tails
- *   are masked), K a multiple of 128 and below 2^24 (at most 2^24 - 128).
+ *   are masked) up to 2^36 each, K a multiple of 128 and below 2^24 (at most 2^24 - 128).
  *   workspace / workspace_bytes: optional device scratch (16-byte aligned) for a split-K
  *   schedule, used by shapes with too few output tiles to fill the GPU; pass NULL / 0 to run
  *   without it. If workspace_bytes is smaller than fp8_block_gemm_workspace_bytes() the call
@@ -175,8 +175,8 @@ int fp8_block_gemm_bias(const uint8_t *aq, const float *sa, const uint8_t *wq, c
  *      accumulator).                            4-byte aligned.
  *   Every product is exact in fp32; the products are summed in fp32 by the bf16 matrix
  *   unit, 32 at a time, the partial sums chained in fp32 along K. M, N >= 0 arbitrary
- *   (ragged tails masked); K a multiple of 64 below 2^23 (FP8Q_ERR_SHAPE otherwise). With
- *   K = 0 the output is the bias (or zeros). */
+ *   (ragged tails masked), M and N up to 2^36; K a multiple of 64 below 2^23 (FP8Q_ERR_SHAPE
+ *   otherwise). With K = 0 the output is the bias (or zeros). */
 int fp8_bf16_gemm(const uint16_t *x, const uint16_t *w, const float *bias, void *y, int y_dtype,
                   int64_t M, int64_t N, int64_t K, void *stream);
 

@@ -139,6 +139,10 @@ def test_block_gemm_validation(lib):
     assert call(M=1 << 30, N=1 << 30) == L.FP8Q_ERR_SHAPE
     # K below 2^24: a 256-row tile's byte range (256 K) must be stated in 32 bits
     assert call(K=1 << 24) == L.FP8Q_ERR_SHAPE
+    # row and column counts up to 2^36 (tile counts stay within 32-bit ints), even where
+    # M * N and M * K are within the element limit
+    assert call(M=(1 << 38) + 128, N=128, K=128) == L.FP8Q_ERR_SHAPE
+    assert call(M=128, N=(1 << 36) + 1, K=128) == L.FP8Q_ERR_SHAPE
     assert lib.fp8_block_gemm_workspace_bytes(4, 4, 1 << 24, L.FP8Q_OUT_BF16) == 0
     assert lib.fp8_block_gemm_workspace_bytes(4096, 576, 7168, L.FP8Q_OUT_BF16) >= 0
     assert lib.fp8_block_gemm_workspace_bytes(4, 4, 100, L.FP8Q_OUT_BF16) == 0
@@ -172,6 +176,7 @@ def test_bf16_gemm_validation(lib):
     assert call(dt=7) == L.FP8Q_ERR_DTYPE
     assert call(K=96) == L.FP8Q_ERR_SHAPE
     assert call(K=1 << 23) == L.FP8Q_ERR_SHAPE
+    assert call(M=(1 << 38) + 64, N=64, K=64) == L.FP8Q_ERR_SHAPE
     assert call(M=-1) == L.FP8Q_ERR_SHAPE
     assert call(N=-1) == L.FP8Q_ERR_SHAPE
     assert call(y=None) == L.FP8Q_ERR_NULL
