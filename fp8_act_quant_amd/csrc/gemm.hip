@@ -684,6 +684,14 @@ __global__ __launch_bounds__(NW * 64) void block_gemm_kernel(GemmArgs g) {
 #pragma unroll
             for (int j = 0; j < SUB_N; ++j) promote(acc[SUB_M - 1][j], p_prev[j], f_prev[j]);
         } else {
+            // Promotion lag. A row group's SUB_N slice partials are normally promoted during the
+            // next row group's MFMAs. A wave tile of 32 or more blocks (the exact-slice 256x256
+            // tile, 128x64 per wave) has no registers for them beside its accumulators, so there
+            // each block's partial is promoted during the next block's MFMAs, and a row group's
+            // last one during the next row group's first block: one partial is carried instead
+            // of SUB_N. Each output's promotions keep their slice order either way, so the
+            // result is the same bit for bit.
+            constexpr bool CARRY_ONE = EXACT && SUB_M * SUB_N >= 32;
             // fragments of the slice being contracted
             i32x8 wf[SUB_N];
             Frag16 wh[EXACT ? SUB_N : 1];
@@ -770,7 +778,12 @@ __global__ __launch_bounds__(NW * 64) void block_gemm_kernel(GemmArgs g) {
                             p_cur[j] = mfma_slice_exact(wh[j], ah);
                             if (copy_now && i < COPY_GROUPS) dma.issue_part(copy_dst, kb + NSTAGE - 1, i * SUB_N + j);
                             if (head_now) wf[j] = frag_at(next + 16 * j * G_SLICE, w_lo, w_hi);
-                            promote(acc[ip][j], p_prev[j], f_prev[j]);
+                            if constexpr (CARRY_ONE) {
+                                if (j > 0) promote(acc[i][j - 1], p_cur[j - 1], f_cur[j - 1]);
+                                else promote(acc[ip][SUB_N - 1], p_prev[0], f_prev[0]);
+                            } else {
+                                promote(acc[ip][j], p_prev[j], f_prev[j]);
+                            }
                             // the four f16 MFMAs interleaved with the promotion FMAs (and, in the
                             // first block, the tail of the A conversion), two VALU instructions
                             // after each MFMA (measured: 2% faster than the compiler's own order
@@ -781,6 +794,10 @@ __global__ __launch_bounds__(NW * 64) void block_gemm_kernel(GemmArgs g) {
                                 __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);   // two VALU
                             });
                             __builtin_amdgcn_sched_barrier(0);
+                        }
+                        if constexpr (CARRY_ONE) {   // the row group's last partial
+                            p_prev[0] = p_cur[SUB_N - 1];
+                            f_prev[0] = f_cur[SUB_N - 1];
                         }
                         if (head_now) {
     #pragma unroll
@@ -803,10 +820,12 @@ __global__ __launch_bounds__(NW * 64) void block_gemm_kernel(GemmArgs g) {
                         lds_barrier();
                         load_slice_head(next);
                     }
+                    if constexpr (!CARRY_ONE) {
     #pragma unroll
-                    for (int j = 0; j < SUB_N; ++j) {
-                        p_prev[j] = p_cur[j];
-                        f_prev[j] = f_cur[j];
+                        for (int j = 0; j < SUB_N; ++j) {
+                            p_prev[j] = p_cur[j];
+                            f_prev[j] = f_cur[j];
+                        }
                     }
                     if (i + 1 < SUB_M || head_now) {
                         af = af_n;
@@ -842,8 +861,12 @@ __global__ __launch_bounds__(NW * 64) void block_gemm_kernel(GemmArgs g) {
                     st = st_next;
                 }
             }
+            if constexpr (CARRY_ONE) {
+                promote(acc[SUB_M - 1][SUB_N - 1], p_prev[0], f_prev[0]);
+            } else {
 #pragma unroll
-            for (int j = 0; j < SUB_N; ++j) promote(acc[SUB_M - 1][j], p_prev[j], f_prev[j]);
+                for (int j = 0; j < SUB_N; ++j) promote(acc[SUB_M - 1][j], p_prev[j], f_prev[j]);
+            }
         }
     }
 
@@ -1005,7 +1028,9 @@ __global__ __launch_bounds__(NW * 64) void block_gemm_kernel(GemmArgs g) {
 // Tile configurations: (BM, BN, waves, waves along M, stages). The timing columns are
 // measured on MI355X (bf16 output, 512 tiles on 256 CUs, K = 1024 and 4096), per
 // contraction mode: the duration of one K slice of one tile, and the fixed cost of a tile
-// (first copies in flight, output stores).
+// (first copies in flight, output stores). The exact-slice columns of 256x256w8 were measured
+// later on one box beside 256x128w8, 128x256w8 and 128x192w8 (fp32 output, same shapes) and
+// scaled by the ratio of those three tiles' slice times to their columns here.
 enum GemmTile {
     T256x256W8 = 0, T256x192W8, T256x128W8, T128x256W8, T128x192W8, T256x128, T128x128, T128x128S2,
     T_COUNT
@@ -1021,7 +1046,7 @@ struct TileInfo {
 };
 
 static const TileInfo kTiles[T_COUNT] = {
-    {"256x256w8", 256, 256, true, false, 1.74, 11.1, 0, 0, 0},
+    {"256x256w8", 256, 256, true, true, 1.74, 11.1, 3.73, 13.4, 0},
     {"256x192w8", 256, 192, true, false, 1.51, 7.1, 0, 0, 0},
     {"256x128w8", 256, 128, true, true, 1.00, 7.8, 2.04, 5.9, 1},
     {"128x256w8", 128, 256, true, true, 0.91, 7.9, 2.10, 4.7, 1},
@@ -1241,6 +1266,7 @@ static hipError_t launch_cfg(GemmArgs a, bool out_bf16, int splits, hipStream_t 
 static hipError_t dispatch(const GemmPlan &p, const GemmArgs &a, bool out_bf16, bool exact, hipStream_t stream) {
     if (exact) {
         switch (p.tile) {
+        case T256x256W8: return launch_cfg<256, 256, 8, 2, 2, 1>(a, out_bf16, 1, stream);
         case T256x128W8: return launch_cfg<256, 128, 8, 4, 3, 1>(a, out_bf16, 1, stream);
         case T128x256W8: return launch_cfg<128, 256, 8, 2, 3, 1>(a, out_bf16, 1, stream);
         case T128x192W8: return launch_cfg<128, 192, 8, 2, 3, 1>(a, out_bf16, 1, stream);

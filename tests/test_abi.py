@@ -231,12 +231,14 @@ def test_gemm_plans_of_the_workloads(lib):
     assert plan(4096, 576, 7168, bf16) == ("128x192w8", 2)
     assert plan(4096, 576, 7168, f32) == ("128x128", 1)
     assert plan(8192, 32768, 512, bf16) == ("256x256w8", 1)
-    assert plan(16384, 7168, 7168, f32) == ("256x128w8", 1)
+    assert plan(16384, 7168, 7168, f32) == ("256x256w8", 1)
     assert plan(16384, 7168, 7168, f32 | L.FP8Q_GEMM_FP8_PRODUCTS) == ("256x256w8", 1)
     try:
         assert lib.fp8q_gemm_force_config(names.index("256x256w8"), 0) == L.FP8Q_OK
         assert plan(4096, 1536, 7168, bf16)[0] == "256x256w8"      # (split count: the planner's)
-        assert plan(4096, 1536, 7168, f32) == ("128x128", 1)      # no exact-slice 256x256: the default
+        assert plan(4096, 1536, 7168, f32) == ("256x256w8", 1)
+        assert lib.fp8q_gemm_force_config(names.index("256x192w8"), 0) == L.FP8Q_OK
+        assert plan(4096, 1536, 7168, f32) == ("128x128", 1)      # no exact-slice 256x192: the default
         assert lib.fp8q_gemm_force_config(names.index("256x256w8"), 1) == L.FP8Q_OK
         assert plan(4096, 1536, 7168, bf16) == ("256x256w8", 1)
     finally:

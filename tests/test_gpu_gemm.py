@@ -377,8 +377,8 @@ def test_gemm_kmajor_scales_every_tile(M, N, K):
 
 def test_gemm_maximum_k():
     """The largest K the ABI takes (2^24 - 128, 131071 slices) with 256-row tiles, whose
-    row offsets into A reach 255 * K + K - 16, just below 2^32: forced 256x128 (exact slices,
-    fp32 out, and FP8 products, bf16 out) and 256x256 (FP8 products), plus the planner's choice
+    row offsets into A reach 255 * K + K - 16, just below 2^32: forced 256x128 and 256x256 (exact
+    slices, fp32 out, and FP8 products, bf16 out), plus the planner's choice
     with a split-K workspace, each against the oracle on sampled outputs that include the last
     row of the 256-row tile and the ragged last column. (The K limit itself: test_abi.)"""
     from fp8_act_quant_amd import _lib as L
@@ -402,7 +402,7 @@ def test_gemm_maximum_k():
     names = _configs()
     ws = torch.zeros(64 << 20, dtype=torch.uint8, device="cuda")
     cases = [("256x128w8", "f32", "exact"), ("256x128w8", "bf16", "fp8"), ("256x256w8", "bf16", "fp8"),
-             (None, "bf16", "fp8"), (None, "f32", "exact")]
+             ("256x256w8", "f32", "exact"), (None, "bf16", "fp8"), (None, "f32", "exact")]
     try:
         for name, out, mode in cases:
             assert fq.lib.fp8q_gemm_force_config(names.index(name) if name else -1, 1 if name else 0) == L.FP8Q_OK
