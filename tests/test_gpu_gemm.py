@@ -303,6 +303,33 @@ def test_gemm_every_tile_configuration(M, N, K):
         fq.lib.fp8q_gemm_force_config(-1, 0)
 
 
+def test_gemm_tiles_agree_bitwise():
+    """Without split-K every tile configuration forms each output by the same arithmetic (the
+    slices in K order, each slice partial from the same matrix-unit instructions, one fp32
+    promotion FMA per slice), so all configurations must give the same bits, in each
+    contraction mode; the tiles differ only in which workgroup and wave compute an output
+    (and, on the exact-slice 256x256 tile, in when a block's promotion is issued)."""
+    from fp8_act_quant_amd import _lib as L
+    M, N, K = 300, 576, 2048
+    A = synth.random_bf16((M, K), seed=31337)
+    W = synth.random_bf16((N, K), seed=31338, std=0.02)
+    aq, sa, wq, sw = quantise_on_gpu(A, W)
+    try:
+        for out, mode in (("f32", "exact"), ("bf16", "fp8"), ("f32", "fp8"), ("bf16", "exact")):
+            first = None
+            for c, name in enumerate(_configs()):
+                assert fq.lib.fp8q_gemm_force_config(c, 1) == L.FP8Q_OK
+                y = fq.fp8_gemm(aq, sa, wq, sw, out_dtype=TORCH_OUT[out], mode=mode, workspace=None)
+                torch.cuda.synchronize()
+                bits = y.view(torch.int32 if out == "f32" else torch.int16).cpu()
+                if first is None:
+                    first = (name, bits)
+                else:
+                    assert torch.equal(bits, first[1]), (name, first[0], out, mode)
+    finally:
+        fq.lib.fp8q_gemm_force_config(-1, 0)
+
+
 @pytest.mark.parametrize("nkb", [1, 2, 3, 4, 5, 6, 7, 8, 9, 14, 15])
 def test_gemm_every_tile_every_slice_count(nkb):
     """Every tile configuration at every short slice count: the K loops are unrolled by
