@@ -330,6 +330,31 @@ def test_gemm_tiles_agree_bitwise():
         fq.lib.fp8q_gemm_force_config(-1, 0)
 
 
+def test_gemm_bias_every_tile_bitwise():
+    """The fused bias of every tile configuration's epilogue, bit for bit: the kernel adds the
+    bias row to the fp32 accumulator once, before the output rounding, so with fp32 output the
+    result equals the unbiased fp32 output plus the bias in fp32, and the bf16 output equals
+    that sum rounded to bf16 (round to nearest even), in both contraction modes."""
+    from fp8_act_quant_amd import _lib as L
+    M, N, K = 300, 576, 2048
+    A = synth.random_bf16((M, K), seed=4242)
+    W = synth.random_bf16((N, K), seed=4243, std=0.02)
+    aq, sa, wq, sw = quantise_on_gpu(A, W)
+    b = torch.from_numpy(np.random.Generator(np.random.PCG64(4244)).standard_normal(N).astype(np.float32)).cuda()
+    try:
+        for c, name in enumerate(_configs()):
+            assert fq.lib.fp8q_gemm_force_config(c, 1) == L.FP8Q_OK
+            for mode in ("exact", "fp8"):
+                y32 = fq.fp8_gemm(aq, sa, wq, sw, out_dtype=torch.float32, mode=mode, workspace=None)
+                y32b = fq.fp8_gemm(aq, sa, wq, sw, out_dtype=torch.float32, mode=mode, workspace=None, bias=b)
+                y16b = fq.fp8_gemm(aq, sa, wq, sw, out_dtype=torch.bfloat16, mode=mode, workspace=None, bias=b)
+                torch.cuda.synchronize()
+                assert torch.equal((y32 + b).view(torch.int32), y32b.view(torch.int32)), (name, mode, "fp32")
+                assert torch.equal(y32b.to(torch.bfloat16).view(torch.int16), y16b.view(torch.int16)), (name, mode, "bf16")
+    finally:
+        fq.lib.fp8q_gemm_force_config(-1, 0)
+
+
 @pytest.mark.parametrize("nkb", [1, 2, 3, 4, 5, 6, 7, 8, 9, 14, 15])
 def test_gemm_every_tile_every_slice_count(nkb):
     """Every tile configuration at every short slice count: the K loops are unrolled by
